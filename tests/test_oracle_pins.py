@@ -1,0 +1,429 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+* brute force: every expert evaluated densely for every token with plain Python
+  loops, selection by rank counting (tests/helpers.py);
+* closed forms and special cases (zero router, k = E, k = 1, zero down
+  projections, x = 0, E = k = 1, scaling and permutation symmetries);
+* hand-derived single-channel values (derivations in the comments);
+* the stated constants and the parameter counts of the "Laguna-M.1-base" card
+  (tests/golden/page_facts.json);
+* the invariant checker rejects corrupted orders.
+
+``test_planted_mistakes_are_caught`` plants plausible mistakes in the oracle
+(on the CPU) and checks that the battery fails for each.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from tests.helpers import ArrayInputs, brute_force_layer, random_inputs, rank_count_select
+from mixture_experts_transformer_moe_amd import configs, inputs as gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _facts():
+    with open(os.path.join(GOLDEN, "page_facts.json")) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- brute force
+
+BRUTE_CASES = [
+    # (seed, T, D, E, F, Fs, k, bias)
+    (0, 6, 5, 4, 3, 2, 2, False),
+    (1, 5, 3, 6, 2, 0, 3, True),
+    (2, 7, 4, 5, 4, 3, 5, False),     # k = E
+    (3, 4, 6, 3, 2, 2, 1, True),      # k = 1
+    (4, 3, 4, 1, 3, 0, 1, False),     # E = 1
+    (5, 8, 2, 7, 5, 4, 4, True),
+]
+
+
+def _check_brute(case, oracle=O, alpha=2.5):
+    seed, T, D, E, F, Fs, k, bias = case
+    rng = np.random.default_rng(100 + seed)
+    inp = random_inputs(rng, T, D, E, F, Fs, bias=bias)
+    out, r = oracle.forward(inp, alpha, k)
+    ref, chosen, weights = brute_force_layer(inp, k, alpha)
+    ref = np.array(ref)
+    if [set(map(int, row)) for row in r.topk_idx] != chosen:
+        return False
+    for t in range(T):
+        for j in range(k):
+            if abs(r.topk_w[t, j] - weights[t][int(r.topk_idx[t, j])]) > 1e-12:
+                return False
+    return bool(np.allclose(out, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max()))
+
+
+@pytest.mark.parametrize("case", BRUTE_CASES)
+def test_oracle_matches_brute_force(case):
+    assert _check_brute(case)
+
+
+def test_brute_force_on_bf16_storage():
+    rng = np.random.default_rng(7)
+    T, D, E, F, Fs, k = 5, 8, 6, 4, 4, 3
+    f = lambda *s: gen.f32_to_bf16_bits((rng.standard_normal(s) * 0.4).astype(np.float32))
+    inp = ArrayInputs(f(T, D), f(E, D), None, f(E, 2 * F, D), f(E, D, F), (f(2 * Fs, D), f(D, Fs)))
+    out, _ = O.forward(inp, 2.5, k)
+    ref = np.array(brute_force_layer(inp, k, 2.5)[0])
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_selection_equals_rank_counting_with_ties():
+    rng = np.random.default_rng(11)
+    # many exact ties: logits drawn from a handful of values, including both zeros
+    vals = np.array([-1.5, -0.0, 0.0, 0.25, 0.25, 3.0])
+    for _ in range(200):
+        E = int(rng.integers(1, 10))
+        k = int(rng.integers(1, E + 1))
+        z = rng.choice(vals, size=(1, E))
+        assert O.select_topk(z, k)[0].tolist() == rank_count_select(z[0].tolist(), k)
+
+
+def test_forward_tokens_matches_forward():
+    shape = configs.variant(configs.TINY_F32, T=24)
+    inp = gen.LayerInputs(shape)
+    out, r = O.forward(inp, shape.alpha, shape.k)
+    toks = [0, 5, 23, 11]
+    np.testing.assert_allclose(O.forward_tokens(inp, shape.alpha, r, toks), out[toks], rtol=1e-12,
+                               atol=1e-15)
+
+
+# ------------------------------------------------------------- closed forms
+
+def _inputs(x, wr, b, wgu, wd, sh=None):
+    f = lambda a: None if a is None else np.asarray(a, dtype=np.float64)
+    return ArrayInputs(f(x), f(wr), None if b is None else np.asarray(b, np.float32), f(wgu), f(wd),
+                       None if sh is None else (f(sh[0]), f(sh[1])))
+
+
+def test_zero_router_picks_lowest_indices_with_equal_weights():
+    rng = np.random.default_rng(1)
+    T, D, E, F, k = 4, 3, 6, 2, 3
+    inp = random_inputs(rng, T, D, E, F, 0)
+    inp.w_router = np.zeros((E, D))
+    _, r = O.forward(inp, 2.5, k)
+    assert (r.topk_idx == np.arange(k)).all()
+    np.testing.assert_allclose(r.topk_w, 1.0 / k, rtol=0, atol=1e-15)
+
+
+def test_k_equals_E_gives_sigmoid_share():
+    rng = np.random.default_rng(2)
+    z = rng.standard_normal((3, 5)) * 2
+    r = O.route(z, 5)
+    for t in range(3):
+        s = [1 / (1 + math.exp(-v)) for v in z[t]]
+        for j in range(5):
+            e = r.topk_idx[t, j]
+            assert abs(r.topk_w[t, j] - s[e] / sum(s)) < 1e-14
+
+
+def test_k1_output_is_shared_plus_scaled_argmax_expert():
+    rng = np.random.default_rng(3)
+    inp = random_inputs(rng, 5, 4, 5, 3, 2)
+    out, r = O.forward(inp, 2.5, 1)
+    for t in range(5):
+        z = O.widen(inp.x[t]) @ O.widen(inp.w_router).T
+        e = int(np.argmax(z))
+        y = O.swiglu_expert(inp.x[t:t + 1], *inp.expert(e))[0]
+        ysh = O.swiglu_expert(inp.x[t:t + 1], *inp.shared())[0]
+        assert np.allclose(out[t], ysh + 2.5 * y, rtol=1e-13, atol=1e-15)
+        assert abs(r.topk_w[t, 0] - 1.0) < 1e-15
+
+
+def test_zero_down_projection_leaves_shared_only_and_vice_versa():
+    rng = np.random.default_rng(4)
+    T, D, E, F, Fs, k = 6, 4, 5, 3, 3, 2
+    inp = random_inputs(rng, T, D, E, F, Fs)
+    sh_out = O.swiglu_expert(inp.x, *inp.shared())
+    inp0 = ArrayInputs(inp.x, inp.w_router, None, inp._wgu, np.zeros_like(inp._wd), inp.shared())
+    assert np.array_equal(O.forward(inp0, 2.5, k)[0], sh_out)
+    inp1 = ArrayInputs(inp.x, inp.w_router, None, inp._wgu, inp._wd,
+                       (inp.shared()[0], np.zeros_like(inp.shared()[1])))
+    inp2 = ArrayInputs(inp.x, inp.w_router, None, inp._wgu, inp._wd, None)
+    np.testing.assert_allclose(O.forward(inp1, 2.5, k)[0], O.forward(inp2, 2.5, k)[0], rtol=0, atol=0)
+
+
+def test_zero_input_gives_zero_output():
+    rng = np.random.default_rng(5)
+    inp = random_inputs(rng, 3, 4, 4, 2, 2, bias=True)
+    inp.x = np.zeros_like(inp.x)
+    out, r = O.forward(inp, 2.5, 2)
+    assert np.array_equal(out, np.zeros_like(out))
+
+
+def test_linear_in_down_projections_and_alpha_on_routed_only():
+    rng = np.random.default_rng(6)
+    inp = random_inputs(rng, 5, 4, 4, 3, 2)
+    out, _ = O.forward(inp, 2.5, 2)
+    inp2 = ArrayInputs(inp.x, inp.w_router, None, inp._wgu, 2 * inp._wd, (inp.shared()[0], 2 * inp.shared()[1]))
+    np.testing.assert_allclose(O.forward(inp2, 2.5, 2)[0], 2 * out, rtol=1e-14, atol=0)
+    # out(alpha) is affine in alpha with slope = routed sum and intercept = shared
+    o0 = O.forward(inp, 0.0, 2)[0]
+    o1 = O.forward(inp, 1.0, 2)[0]
+    np.testing.assert_allclose(o0, O.swiglu_expert(inp.x, *inp.shared()), rtol=1e-14, atol=1e-16)
+    np.testing.assert_allclose(out, o0 + 2.5 * (o1 - o0), rtol=1e-12, atol=1e-14)
+
+
+def test_token_permutation_equivariance():
+    rng = np.random.default_rng(8)
+    inp = random_inputs(rng, 9, 4, 6, 3, 2, bias=True)
+    out, r = O.forward(inp, 2.5, 3)
+    p = rng.permutation(9)
+    inp_p = ArrayInputs(inp.x[p], inp.w_router, inp.bias, inp._wgu, inp._wd, inp.shared())
+    out_p, r_p = O.forward(inp_p, 2.5, 3)
+    np.testing.assert_allclose(out_p, out[p], rtol=1e-13, atol=1e-15)
+    assert np.array_equal(r_p.topk_idx, r.topk_idx[p])
+
+
+def test_single_expert_is_scaled_dense_swiglu():
+    # E = k = 1, no shared expert: out = alpha * Wd (silu(Wg x) * Wu x), with the
+    # dense SwiGLU written out element by element here.
+    rng = np.random.default_rng(9)
+    T, D, F = 3, 4, 5
+    inp = random_inputs(rng, T, D, 1, F, 0)
+    out, r = O.forward(inp, 2.5, 1)
+    wgu, wd = inp.expert(0)
+    for t in range(T):
+        for d in range(D):
+            acc = 0.0
+            for f in range(F):
+                g = sum(wgu[f, i] * inp.x[t, i] for i in range(D))
+                u = sum(wgu[F + f, i] * inp.x[t, i] for i in range(D))
+                acc += wd[d, f] * (g / (1 + math.exp(-g))) * u
+            assert abs(out[t, d] - 2.5 * acc) < 1e-12
+
+
+# ------------------------------------------------------ hand-derived values
+
+LN3 = math.log(3.0)
+
+
+def test_hand_sigmoid_renormalisation():
+    # One channel, x = 1, two experts with logits ln 3 and 0:
+    # sigma(ln 3) = 1 / (1 + 1/3) = 3/4 and sigma(0) = 1/2, so renormalised
+    # weights are (3/4)/(5/4) = 3/5 and (1/2)/(5/4) = 2/5.  (A softmax would give
+    # 3/4 and 1/4.)
+    r = O.route(np.array([[LN3, 0.0]]), 2)
+    assert r.topk_idx.tolist() == [[0, 1]]
+    assert abs(r.topk_w[0, 0] - 0.6) < 1e-15 and abs(r.topk_w[0, 1] - 0.4) < 1e-15
+
+
+def test_hand_swiglu_branch_order():
+    # D = F = 1, x = 1, gate weight ln 3, up weight 2, down weight 1:
+    # silu(ln 3) * 2 = ln 3 * 3/4 * 2 = 1.5 ln 3 = 1.6479184330021646.
+    # (Swapping the branches would give silu(2) * ln 3 = 1.9353...)
+    y = O.swiglu_expert(np.array([[1.0]]), np.array([[LN3], [2.0]]), np.array([[1.0]]))
+    assert abs(y[0, 0] - 1.5 * LN3) < 1e-15
+
+
+def test_hand_full_layer_two_experts_and_shared():
+    # D = F = Fs = 1, x = 1, E = 2, k = 1, alpha = 2.5.
+    # Router rows [0.5], [-0.5] -> expert 0 wins with weight 1.
+    # Expert 0: gate 0, up 3, down 1 -> silu(0) * 3 = 0, so the routed part is 0.
+    # Shared: gate ln 3, up 1, down 2 -> 2 * (3/4) ln 3 = 1.5 ln 3.
+    # out = 1.5 ln 3 + 2.5 * 0.
+    inp = _inputs([[1.0]], [[0.5], [-0.5]], None, [[[0.0], [3.0]], [[1.0], [1.0]]],
+                  [[[1.0]], [[1.0]]], ([[LN3], [1.0]], [[2.0]]))
+    out, r = O.forward(inp, 2.5, 1)
+    assert r.topk_idx.tolist() == [[0]]
+    assert abs(out[0, 0] - 1.5 * LN3) < 1e-15
+    # Flip the router: expert 1 (gate 1, up 1, down 1): silu(1) = sigma(1) = 1/(1+e^-1).
+    inp.w_router = np.array([[-0.5], [0.5]])
+    out, r = O.forward(inp, 2.5, 1)
+    assert r.topk_idx.tolist() == [[1]]
+    assert abs(out[0, 0] - (1.5 * LN3 + 2.5 / (1 + math.exp(-1.0)))) < 1e-15
+
+
+def test_hand_bias_enters_selection_and_weight():
+    # Zero router, bias (0, 5, 0, 3), k = 2: experts 1 then 3; weights
+    # sigma(5) / (sigma(5) + sigma(3)) and sigma(3) / (sigma(5) + sigma(3)).
+    inp = _inputs([[1.0, -2.0]], np.zeros((4, 2)), [0, 5, 0, 3], np.ones((4, 2, 2)),
+                  np.ones((4, 2, 1)))
+    _, r = O.forward(inp, 2.5, 2)
+    assert r.topk_idx.tolist() == [[1, 3]]
+    s5, s3 = 1 / (1 + math.exp(-5)), 1 / (1 + math.exp(-3))
+    assert abs(r.topk_w[0, 0] - s5 / (s5 + s3)) < 1e-15
+
+
+def test_signed_zero_and_ties_go_to_lower_index():
+    r = O.route(np.array([[-0.0, 0.0, -0.0, -1.0]]), 3)
+    assert r.topk_idx.tolist() == [[0, 1, 2]]
+    r = O.route(np.array([[1.0, 2.0, 2.0, 1.0]]), 3)
+    assert r.topk_idx.tolist() == [[1, 2, 0]]
+
+
+def test_non_finite_logits_raise():
+    with pytest.raises(ValueError):
+        O.route(np.array([[0.0, np.nan]]), 1)
+
+
+def test_expert_order_hand_case():
+    # tokens 0..2 with k = 2 over 3 experts
+    idx = np.array([[2, 0], [0, 1], [2, 1]], dtype=np.int32)
+    counts, offsets, st, slot = O.expert_order(idx, 3)
+    assert counts.tolist() == [2, 2, 2]
+    assert offsets.tolist() == [0, 2, 4, 6]
+    assert st.tolist() == [0, 1, 1, 2, 0, 2]
+    assert slot.tolist() == [[4, 0], [1, 2], [5, 3]]
+
+
+# ------------------------------------------------------------- invariants
+
+def test_invariants_hold_on_small_workload_and_catch_corruption():
+    shape = configs.TINY_F32
+    inp = gen.LayerInputs(shape)
+    out, r = O.forward(inp, shape.alpha, shape.k)
+    args = (r.topk_idx, r.topk_w, r.counts, r.offsets, r.sorted_token, r.slot_of, shape.E)
+    O.check_invariants(*args)
+    for which, mutate in [
+        (5, lambda a: a.__setitem__((0, 0), a[0, 1])),           # slot_of not a bijection
+        (4, lambda a: a.__setitem__(slice(0, 2), a[1::-1])),     # segment out of order
+        (2, lambda a: a.__setitem__(0, a[0] + 1)),               # counts off by one
+        (0, lambda a: a.__setitem__((0, 1), a[0, 0])),           # duplicate expert
+        (1, lambda a: a.__setitem__((0, 0), a[0, 0] * 1.01)),    # weights do not sum to 1
+    ]:
+        b = [x.copy() if isinstance(x, np.ndarray) else x for x in args]
+        mutate(b[which])
+        with pytest.raises(AssertionError):
+            O.check_invariants(*b)
+
+
+# ------------------------------------------------------------ page constants
+
+def test_workload_constants_match_pages():
+    f = _facts()
+    for s in configs.WORKLOADS.values():
+        if s.dtype == "bf16":
+            assert s.E == f["routed_experts"]["value"]
+            assert s.k == f["xs2_top_k"]["value"]
+        assert s.alpha == f["xs2_routed_scale"]["value"]
+        assert s.Fs == s.F                                      # one shared expert per layer
+    assert configs.M1_T8192.D == f["m1_d_model"]["value"]
+    assert configs.M1_T8192.F == f["m1_expert_dim"]["value"]
+
+
+def _m1_counts(shared=True, out_gate=True, k=16):
+    f = _facts()
+    D = f["m1_d_model"]["value"]
+    E = f["routed_experts"]["value"]
+    F = f["m1_expert_dim"]["value"]
+    hq, hkv, hd = f["m1_q_heads"]["value"], f["m1_kv_heads"]["value"], f["m1_head_dim"]["value"]
+    L, Ld = f["m1_layers"]["value"], f["m1_leading_dense_layers"]["value"]
+    V, Fd = f["vocab"]["value"], f["m1_dense_ffn_dim"]["value"]
+    attn = D * hq * hd + 2 * D * hkv * hd + hq * hd * D + (D * hq * hd if out_gate else 0) + 2 * hd
+    norms = 2 * D
+    expert = 3 * D * F                     # SwiGLU: gate, up, down; no biases
+    moe = attn + norms + E * D + E * expert + (expert if shared else 0)
+    dense = attn + norms + 3 * D * Fd
+    emb = 2 * V * D                        # untied
+    total = (L - Ld) * moe + Ld * dense + emb + D
+    active_non_emb = (L - Ld) * (moe - E * expert + k * expert) + Ld * dense + D
+    return dict(total=total, largest=moe, active_non_emb=active_non_emb, emb=emb,
+                active=active_non_emb + emb)
+
+
+def test_m1_parameter_counts_reproduce_card():
+    f = _facts()
+    c = _m1_counts()
+    assert round(c["total"] / 1e9, 1) == f["m1_total_params_b"]["value"]
+    assert round(c["largest"] / 1e9, 3) == f["m1_largest_layer_b"]["value"]
+    assert round(c["active_non_emb"] / 1e9, 2) == f["m1_active_non_emb_counted_b"]["value"]
+    assert round(c["emb"] / 1e6, 1) == f["m1_embedding_and_head_m"]["value"]
+    # the publisher's 23.4B (with embeddings) is stated to 0.1B; the counted
+    # 22.64B + 0.822B = 23.46B agrees with it to that precision
+    assert abs(c["active"] / 1e9 - f["m1_active_incl_emb_b"]["value"]) < 0.1
+    # the shared expert and the three-matrix expert are needed to reproduce them
+    assert round(_m1_counts(shared=False)["largest"] / 1e9, 3) != f["m1_largest_layer_b"]["value"]
+    assert round(_m1_counts(k=8)["active_non_emb"] / 1e9, 2) != f["m1_active_non_emb_counted_b"]["value"]
+
+
+# --------------------------------------------------------- oracle digest
+
+def test_small_workload_digest_unchanged():
+    from tests.golden.make_golden import tiny_digest
+    with open(os.path.join(GOLDEN, "tiny_f32_oracle_digest.json")) as f:
+        stored = json.load(f)
+    now = tiny_digest()
+    assert now["topk_idx_sha256"] == stored["topk_idx_sha256"]
+    assert now["sorted_token_sha256"] == stored["sorted_token_sha256"]
+    np.testing.assert_allclose(now["out_samples"], stored["out_samples"], rtol=1e-12, atol=0)
+
+
+# ------------------------------------------------------- planted mistakes
+
+def _battery(oracle) -> bool:
+    """True when every pin above that can see the oracle passes."""
+    try:
+        for case in BRUTE_CASES:
+            if not _check_brute(case, oracle):
+                return False
+        r = oracle.route(np.array([[LN3, 0.0]]), 2)
+        if abs(r.topk_w[0, 0] - 0.6) > 1e-12:
+            return False
+        if oracle.route(np.zeros((1, 5)), 3).topk_idx.tolist() != [[0, 1, 2]]:
+            return False
+        y = oracle.swiglu_expert(np.array([[1.0]]), np.array([[LN3], [2.0]]), np.array([[1.0]]))
+        if abs(y[0, 0] - 1.5 * LN3) > 1e-12:
+            return False
+    except Exception:
+        return False
+    return True
+
+
+def _mut_softmax(z, idx):
+    e = np.exp(np.take_along_axis(np.asarray(z, float), idx.astype(np.int64), axis=1))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def _mut_no_renorm(z, idx):
+    return O.sigmoid(np.take_along_axis(np.asarray(z, float), idx.astype(np.int64), axis=1))
+
+
+def _mut_swap_branches(xrows, wgu, wd):
+    F = wgu.shape[0] // 2
+    return (O.silu(xrows @ wgu[F:].T) * (xrows @ wgu[:F].T)) @ wd.T
+
+
+def _mut_high_index_ties(z, k):
+    z = np.asarray(z, float)
+    E = z.shape[1]
+    order = np.argsort(-z[:, ::-1], axis=1, kind="stable")
+    return (E - 1 - order[:, :k]).astype(np.int32)
+
+
+def _mut_drop_bias(x, w_router, bias):
+    return O.widen(x) @ O.widen(w_router).T
+
+
+def _mut_scale_shared(inputs, xrows64):
+    sh = inputs.shared()
+    if sh is None:
+        return np.zeros_like(xrows64)
+    return 2.5 * O.swiglu_expert(xrows64, O.widen(sh[0]), O.widen(sh[1]))
+
+
+def _mut_relu_gate(xrows, wgu, wd):
+    F = wgu.shape[0] // 2
+    return (np.maximum(xrows @ wgu[:F].T, 0) * (xrows @ wgu[F:].T)) @ wd.T
+
+
+@pytest.mark.parametrize("name,attr,mutant", [
+    ("softmax scores", "renormalised_weights", _mut_softmax),
+    ("no renormalisation", "renormalised_weights", _mut_no_renorm),
+    ("swapped SwiGLU branches", "swiglu_expert", _mut_swap_branches),
+    ("relu instead of silu", "swiglu_expert", _mut_relu_gate),
+    ("ties to higher index", "select_topk", _mut_high_index_ties),
+    ("router bias dropped", "router_logits", _mut_drop_bias),
+    ("alpha on the shared expert", "shared_output", _mut_scale_shared),
+])
+def test_planted_mistakes_are_caught(monkeypatch, name, attr, mutant):
+    assert _battery(O)
+    monkeypatch.setattr(O, attr, mutant)
+    assert not _battery(O), f"pins did not catch: {name}"
