@@ -1,0 +1,172 @@
+/*
+ * moe.h - C ABI of libmoe.so, the MI355X (gfx950) MoE feed-forward layer.
+ *
+ * The layer, per token x_t (width D), as the Laguna pages define it:
+ *   logits   z_t = W_r x_t + b                          ("Laguna M.1/XS.2 Technical
+ *            Report", Key claims: sigmoid router, token-choice top-8 of 256,
+ *            post-top-k normalization, routed output modulated by 2.5 before
+ *            the shared expert is added; report section 3.1)
+ *   select   the k experts first under (z descending, expert index ascending)
+ *   weights  w_j = sigmoid(z_{e_j}) / sum_i sigmoid(z_{e_i})
+ *   experts  y = W_d (silu(W_g x) * (W_u x)), no biases ("Laguna-M.1-base",
+ *            Feed-forward: SwiGLU, FFN bias = no)
+ *   output   out_t = ysh_t + alpha * sum_j w_j y_{t,j}, ysh = the shared expert
+ *
+ * The pages' training system sends tokens to expert owners over NVLink inside a
+ * fused grouped GEMM ("Laguna M.1/XS.2 Technical Report", Key claims: dispatch
+ * and combine fused into the grouped GEMM, report section 3.1.2, Fig. 2).  On
+ * one GPU that exchange becomes an on-device permutation into expert order.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers, allocated and owned by the
+ *     caller, 16-byte aligned, row-major and densely packed.  The library never
+ *     allocates or frees device memory and keeps no device state.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue kernels on it and never synchronise; results are ready when the
+ *     stream has reached that point.  Asynchronous faults surface at the
+ *     caller's next synchronisation.
+ *   - "elem" is 4 bytes (fp32) for MOE_F32 and 2 bytes (bf16 bit patterns)
+ *     for MOE_BF16.  Accumulation is fp32 in both cases.
+ *   - Return value: a moe_status.  Arguments are checked on the host before
+ *     anything is launched; a rejected call enqueues nothing.  The reason of
+ *     the last failure on the calling thread is in moe_last_error().
+ *   - T == 0 is a valid empty batch: the call does nothing and returns MOE_OK.
+ *   - Calls that share output buffers on one stream are ordered by the stream;
+ *     calls on different streams that write the same buffers race.
+ *
+ * Shape limits (else MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED):
+ *   1 <= E <= 256, 1 <= k <= min(E, 16), T >= 0, T * k < 2^31.
+ *   MOE_BF16: D % 128 == 0, F % 64 == 0, Fs % 64 == 0 (Fs == 0 = no shared expert).
+ *   MOE_F32:  D % 4 == 0, F % 4 == 0, Fs % 4 == 0.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* bad shape, null or misaligned pointer */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid layer, but outside this library's limits */
+  MOE_ERR_WORKSPACE = 3,     /* workspace missing or smaller than moe_workspace_bytes */
+  MOE_ERR_HIP = 4            /* a kernel launch failed (hipGetLastError) */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer shape.  T tokens, model width D, E routed experts, k experts per token,
+ * routed SwiGLU width F, shared SwiGLU width Fs (0 = none), routed scale alpha
+ * (2.5 for XS.2, 1 for M.1: "Laguna M.1/XS.2 Technical Report", Key claims;
+ * "Laguna-M.1-base", Mixture of experts: Routed scaling factor), dtype. */
+typedef struct moe_shape {
+  int32_t T, D, E, k, F, Fs;
+  float alpha;
+  int32_t dtype; /* moe_dtype */
+} moe_shape;
+
+/* Library ABI version (this header: 1). */
+int moe_version(void);
+
+/* Static description of a status code.  Never NULL. */
+const char* moe_status_string(int status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none).
+ * The string is thread-local and valid until the next call on that thread. */
+const char* moe_last_error(void);
+
+/* Bytes of device workspace moe_permute needs for this shape (0 on a bad shape).
+ * A multiple of 256. */
+size_t moe_workspace_bytes(const moe_shape* shape);
+
+/* Router: logits, top-k selection and renormalised weights.
+ * Defined by the sigmoid token-choice top-k router with post-top-k
+ * normalisation ("Laguna M.1/XS.2 Technical Report", Key claims; report
+ * section 3.1) -- selection on the fp32 logit, ties to the lower expert index
+ * (-0.0 equals +0.0).
+ *   x         [T, D] elem      layer input (after the pre-norm)
+ *   w_router  [E, D] elem      router weight
+ *   bias      [E] fp32 or NULL additive logit bias (affects selection and weight)
+ *   logits    [T, E] fp32      out: z = x W_r^T + b, the values selection used
+ *   topk_idx  [T, k] int32     out: slot j = j-th expert under the order above
+ *   topk_w    [T, k] fp32      out: sigmoid(z)/sum over the k slots (sums to 1;
+ *                              alpha is NOT applied here)
+ * Non-finite logits are outside the contract: the result is unspecified (still
+ * k distinct in-range experts per token) and nothing faults. */
+int moe_route(const moe_shape* shape, const void* x, const void* w_router, const float* bias,
+              float* logits, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Expert-order permutation: the on-device form of the dispatch all-to-all
+ * (tokens copied "in expert order": "Laguna M.1/XS.2 Technical Report", Key
+ * claims, fused dispatch/grouped GEMM, report section 3.1.2, Fig. 2).
+ *   topk_idx     [T, k] int32   in: from moe_route (values must lie in [0, E))
+ *   x            [T, D] elem    in: layer input
+ *   counts       [E] int32      out: tokens routed to each expert
+ *   offsets      [E+1] int32    out: exclusive scan of counts, offsets[E] = k*T
+ *   sorted_token [k*T] int32    out: expert by expert, the tokens in ascending
+ *                               token order
+ *   slot_of      [T, k] int32   out: position of (t, j) in that order
+ *   x_perm       [k*T, D] elem  out: x_perm[p] = x[sorted_token[p]]; may be NULL
+ *                               to skip the copy
+ *   workspace    >= moe_workspace_bytes(shape) bytes, caller-owned scratch
+ * The result is deterministic (no order depends on timing). */
+int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_token, int32_t* slot_of, void* x_perm,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* First grouped GEMM of the experts with the SwiGLU fused in its epilogue
+ * ("Laguna-M.1-base", Feed-forward: SwiGLU, no bias; the grouped GEMM over
+ * expert-ordered tokens of "Laguna M.1/XS.2 Technical Report", Key claims,
+ * report section 3.1.2).  For each expert e and each of its rows p in
+ * [offsets[e], offsets[e+1]):  h[p] = silu(Wg_e a_p) * (Wu_e a_p)  where a_p is
+ * x_perm[p], or x[sorted_token[p]] when x_perm is NULL.  The shared expert
+ * does the same for every token t:  hs[t] = silu(Wsg x_t) * (Wsu x_t).
+ *   x_perm       [k*T, D] elem or NULL (then sorted_token is read)
+ *   sorted_token [k*T] int32 (read only when x_perm is NULL)
+ *   x            [T, D] elem
+ *   offsets      [E+1] int32 from moe_permute
+ *   w_gate_up    [E, 2F, D] elem: rows 0..F-1 = gate projection, F..2F-1 = up
+ *   ws_gate_up   [2Fs, D] elem, same split; ignored (may be NULL) when Fs == 0
+ *   h            [k*T*F + T*Fs] elem out: routed rows [k*T, F], then shared rows [T, Fs]
+ * The h values are rounded once to elem (bf16 round-to-nearest-even). */
+int moe_grouped_gate_up(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
+                        const void* x, const int32_t* offsets, const void* w_gate_up,
+                        const void* ws_gate_up, void* h, void* stream);
+
+/* Second grouped GEMM: y_perm[p] = Wd_e h[p] for the rows of each expert e, and
+ * y_shared[t] = Wsd hs[t] ("Laguna-M.1-base", Feed-forward: down projection).
+ *   h         as written by moe_grouped_gate_up
+ *   offsets   [E+1] int32
+ *   w_down    [E, D, F] elem
+ *   ws_down   [D, Fs] elem (ignored, may be NULL, when Fs == 0)
+ *   y_perm    [k*T, D] elem out
+ *   y_shared  [T, D] elem out (untouched when Fs == 0; may then be NULL) */
+int moe_grouped_down(const moe_shape* shape, const void* h, const int32_t* offsets,
+                     const void* w_down, const void* ws_down, void* y_perm, void* y_shared,
+                     void* stream);
+
+/* moe_grouped_gate_up followed by moe_grouped_down on the same stream. */
+int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
+                    const void* x, const int32_t* offsets, const void* w_gate_up,
+                    const void* w_down, const void* ws_gate_up, const void* ws_down, void* h,
+                    void* y_perm, void* y_shared, void* stream);
+
+/* Combine: out[t] = y_shared[t] + sum_{j=0..k-1} (alpha * topk_w[t,j]) * y_perm[slot_of[t,j]],
+ * accumulated in fp32 in slot order and rounded once to elem ("Laguna M.1/XS.2
+ * Technical Report", Key claims: routed output modulated by alpha before
+ * combining with the shared expert).
+ *   y_perm    [k*T, D] elem;  y_shared [T, D] elem or NULL (no shared expert)
+ *   slot_of   [T, k] int32;   topk_w [T, k] fp32
+ *   out       [T, D] elem out */
+int moe_combine(const moe_shape* shape, const void* y_perm, const void* y_shared,
+                const int32_t* slot_of, const float* topk_w, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

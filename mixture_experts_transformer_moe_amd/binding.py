@@ -1,0 +1,244 @@
+"""ctypes binding of libmoe.so (argument marshalling only).
+
+Every function here passes ``tensor.data_ptr()`` and the current HIP stream to
+the C entry point of the same name declared in ``include/moe.h``; all
+arithmetic runs in the library's kernels.  PyTorch provides device memory and
+streams.  There is no fallback: a missing library, a CPU tensor or a non-zero
+status raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import torch
+
+from .configs import MoEShape
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+
+# the entry points include/moe.h declares
+EXPORTS = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
+           "moe_route", "moe_permute", "moe_grouped_gate_up", "moe_grouped_down",
+           "moe_grouped_ffn", "moe_combine")
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("D", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("F", ctypes.c_int32), ("Fs", ctypes.c_int32),
+                ("alpha", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_SP = ctypes.POINTER(moe_shape)
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libmoe.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_transformer_moe_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_version.restype = ctypes.c_int
+        L.moe_version.argtypes = []
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_workspace_bytes.argtypes = [_SP]
+        L.moe_route.restype = ctypes.c_int
+        L.moe_route.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_permute.restype = ctypes.c_int
+        L.moe_permute.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_grouped_gate_up.restype = ctypes.c_int
+        L.moe_grouped_gate_up.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_grouped_down.restype = ctypes.c_int
+        L.moe_grouped_down.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_grouped_ffn.restype = ctypes.c_int
+        L.moe_grouped_ffn.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_combine.restype = ctypes.c_int
+        L.moe_combine.argtypes = [_SP, _P, _P, _P, _P, _P, _P]
+        _lib = L
+    return _lib
+
+
+def make_shape(s: MoEShape) -> moe_shape:
+    return moe_shape(s.T, s.D, s.E, s.k, s.F, s.Fs, float(s.alpha),
+                     MOE_BF16 if s.dtype == "bf16" else MOE_F32)
+
+
+def _check(status: int, what: str) -> None:
+    if status != MOE_OK:
+        detail = lib().moe_last_error().decode()
+        raise MoEError(status, f"{what} failed ({lib().moe_status_string(status).decode()}): {detail}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmoe takes device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors only")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def workspace_bytes(shape: moe_shape) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(shape)))
+
+
+def moe_route(shape, x, w_router, bias, logits, topk_idx, topk_w, stream=None):
+    _check(lib().moe_route(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits),
+                           _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "moe_route")
+
+
+def moe_permute(shape, topk_idx, x, counts, offsets, sorted_token, slot_of, x_perm, workspace,
+                stream=None):
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().moe_permute(ctypes.byref(shape), _ptr(topk_idx), _ptr(x), _ptr(counts),
+                             _ptr(offsets), _ptr(sorted_token), _ptr(slot_of), _ptr(x_perm),
+                             _ptr(workspace), nbytes, _stream(stream)), "moe_permute")
+
+
+def moe_grouped_gate_up(shape, x_perm, sorted_token, x, offsets, w_gate_up, ws_gate_up, h,
+                        stream=None):
+    _check(lib().moe_grouped_gate_up(ctypes.byref(shape), _ptr(x_perm), _ptr(sorted_token), _ptr(x),
+                                     _ptr(offsets), _ptr(w_gate_up), _ptr(ws_gate_up), _ptr(h),
+                                     _stream(stream)), "moe_grouped_gate_up")
+
+
+def moe_grouped_down(shape, h, offsets, w_down, ws_down, y_perm, y_shared, stream=None):
+    _check(lib().moe_grouped_down(ctypes.byref(shape), _ptr(h), _ptr(offsets), _ptr(w_down),
+                                  _ptr(ws_down), _ptr(y_perm), _ptr(y_shared), _stream(stream)),
+           "moe_grouped_down")
+
+
+def moe_grouped_ffn(shape, x_perm, sorted_token, x, offsets, w_gate_up, w_down, ws_gate_up, ws_down,
+                    h, y_perm, y_shared, stream=None):
+    _check(lib().moe_grouped_ffn(ctypes.byref(shape), _ptr(x_perm), _ptr(sorted_token), _ptr(x),
+                                 _ptr(offsets), _ptr(w_gate_up), _ptr(w_down), _ptr(ws_gate_up),
+                                 _ptr(ws_down), _ptr(h), _ptr(y_perm), _ptr(y_shared),
+                                 _stream(stream)), "moe_grouped_ffn")
+
+
+def moe_combine(shape, y_perm, y_shared, slot_of, topk_w, out, stream=None):
+    _check(lib().moe_combine(ctypes.byref(shape), _ptr(y_perm), _ptr(y_shared), _ptr(slot_of),
+                             _ptr(topk_w), _ptr(out), _stream(stream)), "moe_combine")
+
+
+# ---------------------------------------------------------------------------
+# buffers and the whole layer
+# ---------------------------------------------------------------------------
+
+def storage_dtype(s: MoEShape) -> torch.dtype:
+    return torch.bfloat16 if s.dtype == "bf16" else torch.float32
+
+
+def to_device(a, s: MoEShape, device) -> torch.Tensor:
+    """Storage-encoded numpy array (fp32, or bf16 bits as uint16) -> device tensor."""
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a.astype(np.float32, copy=False)).to(device)
+
+
+@dataclass
+class LayerBuffers:
+    logits: torch.Tensor
+    topk_idx: torch.Tensor
+    topk_w: torch.Tensor
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    sorted_token: torch.Tensor
+    slot_of: torch.Tensor
+    x_perm: Optional[torch.Tensor]
+    workspace: torch.Tensor
+    h: torch.Tensor
+    y_perm: torch.Tensor
+    y_shared: Optional[torch.Tensor]
+    out: torch.Tensor
+
+
+def alloc_buffers(s: MoEShape, device="cuda", with_x_perm: bool = True) -> LayerBuffers:
+    dt = storage_dtype(s)
+    S = s.S
+    i32 = dict(dtype=torch.int32, device=device)
+    shape_c = make_shape(s)
+    ws = max(workspace_bytes(shape_c), 256)
+    return LayerBuffers(
+        logits=torch.empty((s.T, s.E), dtype=torch.float32, device=device),
+        topk_idx=torch.empty((s.T, s.k), **i32),
+        topk_w=torch.empty((s.T, s.k), dtype=torch.float32, device=device),
+        counts=torch.empty((s.E,), **i32),
+        offsets=torch.empty((s.E + 1,), **i32),
+        sorted_token=torch.empty((S,), **i32),
+        slot_of=torch.empty((s.T, s.k), **i32),
+        x_perm=torch.empty((S, s.D), dtype=dt, device=device) if with_x_perm else None,
+        workspace=torch.empty((ws,), dtype=torch.uint8, device=device),
+        h=torch.empty((S * s.F + s.T * s.Fs,), dtype=dt, device=device),
+        y_perm=torch.empty((S, s.D), dtype=dt, device=device),
+        y_shared=torch.empty((s.T, s.D), dtype=dt, device=device) if s.Fs else None,
+        out=torch.empty((s.T, s.D), dtype=dt, device=device),
+    )
+
+
+@dataclass
+class LayerWeights:
+    w_router: torch.Tensor
+    bias: Optional[torch.Tensor]
+    w_gate_up: torch.Tensor       # [E, 2F, D]
+    w_down: torch.Tensor          # [E, D, F]
+    ws_gate_up: Optional[torch.Tensor]
+    ws_down: Optional[torch.Tensor]
+
+
+def upload(inputs, device="cuda"):
+    """Seeded inputs (``inputs.LayerInputs``) -> (x, LayerWeights) on the device."""
+    s = inputs.shape
+    wgu, wd = inputs.all_experts()
+    sh = inputs.shared()
+    w = LayerWeights(
+        w_router=to_device(inputs.w_router, s, device),
+        bias=None if inputs.bias is None else torch.from_numpy(inputs.bias).to(device),
+        w_gate_up=to_device(wgu, s, device),
+        w_down=to_device(wd, s, device),
+        ws_gate_up=None if sh is None else to_device(sh[0], s, device),
+        ws_down=None if sh is None else to_device(sh[1], s, device),
+    )
+    return to_device(inputs.x, s, device), w
+
+
+def layer_forward(s: MoEShape, x: torch.Tensor, w: LayerWeights, b: LayerBuffers,
+                  stream=None) -> torch.Tensor:
+    """route -> permute -> grouped gate/up + SwiGLU -> grouped down -> combine."""
+    c = make_shape(s)
+    moe_route(c, x, w.w_router, w.bias, b.logits, b.topk_idx, b.topk_w, stream)
+    moe_permute(c, b.topk_idx, x, b.counts, b.offsets, b.sorted_token, b.slot_of, b.x_perm,
+                b.workspace, stream)
+    moe_grouped_gate_up(c, b.x_perm, b.sorted_token, x, b.offsets, w.w_gate_up, w.ws_gate_up, b.h,
+                        stream)
+    moe_grouped_down(c, b.h, b.offsets, w.w_down, w.ws_down, b.y_perm, b.y_shared, stream)
+    moe_combine(c, b.y_perm, b.y_shared, b.slot_of, b.topk_w, b.out, stream)
+    return b.out

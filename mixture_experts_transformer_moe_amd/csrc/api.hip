@@ -1,0 +1,231 @@
+// C ABI of libmoe.so: argument checks on the host, then kernel launches on the
+// caller's stream.  Nothing here allocates device memory or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <cmath>
+
+#include "moe_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define NEED_PTR(p)                                                                 \
+  do {                                                                              \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", #p);         \
+    if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+#define OPT_PTR(p)                                                                  \
+  do {                                                                              \
+    if ((p) != nullptr && !aligned16(p))                                            \
+      return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p);            \
+  } while (0)
+
+// Shape checks common to every entry point.
+int check_shape(const moe_shape* s) {
+  if (s == nullptr) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "dtype %d is neither MOE_F32 nor MOE_BF16", s->dtype);
+  if (s->T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %d < 0", s->T);
+  if (s->E < 1) return fail(MOE_ERR_INVALID_ARG, "E = %d < 1", s->E);
+  if (s->k < 1 || s->k > s->E) return fail(MOE_ERR_INVALID_ARG, "k = %d outside 1..E (E = %d)", s->k, s->E);
+  if (s->D < 1 || s->F < 1 || s->Fs < 0)
+    return fail(MOE_ERR_INVALID_ARG, "D = %d, F = %d, Fs = %d: widths must be positive (Fs >= 0)", s->D, s->F, s->Fs);
+  if (!std::isfinite(s->alpha)) return fail(MOE_ERR_INVALID_ARG, "alpha is not finite");
+  if (s->E > 256) return fail(MOE_ERR_UNSUPPORTED, "E = %d > 256", s->E);
+  if (s->k > 16) return fail(MOE_ERR_UNSUPPORTED, "k = %d > 16", s->k);
+  if (static_cast<int64_t>(s->T) * s->k >= (int64_t{1} << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "k*T = %lld does not fit int32", static_cast<long long>(s->T) * s->k);
+  if (s->dtype == MOE_BF16) {
+    if (s->D % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: D = %d is not a multiple of 128", s->D);
+    if (s->F % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: F = %d is not a multiple of 64", s->F);
+    if (s->Fs % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: Fs = %d is not a multiple of 64", s->Fs);
+  } else {
+    if (s->D % 4 != 0 || s->F % 4 != 0 || s->Fs % 4 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "fp32: D, F and Fs must be multiples of 4");
+    if (s->D > 8192 || s->F > 8192 || s->Fs > 8192)
+      return fail(MOE_ERR_UNSUPPORTED, "fp32: D, F and Fs are limited to 8192");
+  }
+  return MOE_OK;
+}
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return 1; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_workspace_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return moe::permute_workspace_bytes(*shape);
+}
+
+int moe_route(const moe_shape* shape, const void* x, const void* w_router, const float* bias,
+              float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (shape->T == 0) return ok();
+  NEED_PTR(x);
+  NEED_PTR(w_router);
+  OPT_PTR(bias);
+  NEED_PTR(logits);
+  NEED_PTR(topk_idx);
+  NEED_PTR(topk_w);
+  const moe_shape& s = *shape;
+  if (s.dtype == MOE_BF16)
+    return launched(moe::launch_route_bf16(s, static_cast<const moe::bf16_t*>(x),
+                                           static_cast<const moe::bf16_t*>(w_router), bias, logits,
+                                           topk_idx, topk_w, as_stream(stream)));
+  return launched(moe::launch_route_f32(s, static_cast<const float*>(x),
+                                        static_cast<const float*>(w_router), bias, logits, topk_idx,
+                                        topk_w, as_stream(stream)));
+}
+
+int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_token, int32_t* slot_of, void* x_perm,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (shape->T == 0) return ok();
+  NEED_PTR(topk_idx);
+  NEED_PTR(counts);
+  NEED_PTR(offsets);
+  NEED_PTR(sorted_token);
+  NEED_PTR(slot_of);
+  OPT_PTR(x_perm);
+  if (x_perm) NEED_PTR(x);
+  if (workspace == nullptr || !aligned16(workspace))
+    return fail(MOE_ERR_WORKSPACE, "workspace is NULL or not 16-byte aligned");
+  const size_t need = moe::permute_workspace_bytes(*shape);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  return launched(moe::launch_permute(*shape, topk_idx, x, counts, offsets, sorted_token, slot_of,
+                                      x_perm, workspace, as_stream(stream)));
+}
+
+int moe_grouped_gate_up(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
+                        const void* x, const int32_t* offsets, const void* w_gate_up,
+                        const void* ws_gate_up, void* h, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (shape->T == 0) return ok();
+  OPT_PTR(x_perm);
+  if (x_perm == nullptr) NEED_PTR(sorted_token);
+  NEED_PTR(x);
+  NEED_PTR(offsets);
+  NEED_PTR(w_gate_up);
+  if (shape->Fs > 0) NEED_PTR(ws_gate_up);
+  NEED_PTR(h);
+  const moe_shape& s = *shape;
+  if (s.dtype == MOE_BF16)
+    return launched(moe::launch_gate_up_bf16(
+        s, static_cast<const moe::bf16_t*>(x_perm), sorted_token, static_cast<const moe::bf16_t*>(x),
+        offsets, static_cast<const moe::bf16_t*>(w_gate_up),
+        static_cast<const moe::bf16_t*>(ws_gate_up), static_cast<moe::bf16_t*>(h), as_stream(stream)));
+  return launched(moe::launch_gate_up_f32(s, static_cast<const float*>(x_perm), sorted_token,
+                                          static_cast<const float*>(x), offsets,
+                                          static_cast<const float*>(w_gate_up),
+                                          static_cast<const float*>(ws_gate_up),
+                                          static_cast<float*>(h), as_stream(stream)));
+}
+
+int moe_grouped_down(const moe_shape* shape, const void* h, const int32_t* offsets,
+                     const void* w_down, const void* ws_down, void* y_perm, void* y_shared,
+                     void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (shape->T == 0) return ok();
+  NEED_PTR(h);
+  NEED_PTR(offsets);
+  NEED_PTR(w_down);
+  NEED_PTR(y_perm);
+  if (shape->Fs > 0) {
+    NEED_PTR(ws_down);
+    NEED_PTR(y_shared);
+  }
+  const moe_shape& s = *shape;
+  if (s.dtype == MOE_BF16)
+    return launched(moe::launch_down_bf16(
+        s, static_cast<const moe::bf16_t*>(h), offsets, static_cast<const moe::bf16_t*>(w_down),
+        static_cast<const moe::bf16_t*>(ws_down), static_cast<moe::bf16_t*>(y_perm),
+        static_cast<moe::bf16_t*>(y_shared), as_stream(stream)));
+  return launched(moe::launch_down_f32(s, static_cast<const float*>(h), offsets,
+                                       static_cast<const float*>(w_down),
+                                       static_cast<const float*>(ws_down),
+                                       static_cast<float*>(y_perm), static_cast<float*>(y_shared),
+                                       as_stream(stream)));
+}
+
+int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
+                    const void* x, const int32_t* offsets, const void* w_gate_up,
+                    const void* w_down, const void* ws_gate_up, const void* ws_down, void* h,
+                    void* y_perm, void* y_shared, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (shape->T == 0) return ok();
+  // check both halves before launching either
+  OPT_PTR(x_perm);
+  if (x_perm == nullptr) NEED_PTR(sorted_token);
+  NEED_PTR(x);
+  NEED_PTR(offsets);
+  NEED_PTR(w_gate_up);
+  NEED_PTR(w_down);
+  NEED_PTR(h);
+  NEED_PTR(y_perm);
+  if (shape->Fs > 0) {
+    NEED_PTR(ws_gate_up);
+    NEED_PTR(ws_down);
+    NEED_PTR(y_shared);
+  }
+  if (int r = moe_grouped_gate_up(shape, x_perm, sorted_token, x, offsets, w_gate_up, ws_gate_up,
+                                  h, stream))
+    return r;
+  return moe_grouped_down(shape, h, offsets, w_down, ws_down, y_perm, y_shared, stream);
+}
+
+int moe_combine(const moe_shape* shape, const void* y_perm, const void* y_shared,
+                const int32_t* slot_of, const float* topk_w, void* out, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (shape->T == 0) return ok();
+  NEED_PTR(y_perm);
+  OPT_PTR(y_shared);
+  NEED_PTR(slot_of);
+  NEED_PTR(topk_w);
+  NEED_PTR(out);
+  return launched(moe::launch_combine(*shape, y_perm, y_shared, slot_of, topk_w, out,
+                                      as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Combine: out[t] = y_shared[t] + sum_j (alpha * w[t,j]) * y_perm[slot_of[t,j]]
+// ("Laguna M.1/XS.2 Technical Report", Key claims: routed-expert output
+// modulated by 2.5 before combining with the shared expert).  A weighted gather
+// of k expert-ordered rows per token, fp32 accumulation in slot order, one
+// rounding.  HBM-bound: one workgroup per token, 16-byte loads; the shared add
+// is fused.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxK = 16;
+
+__device__ __forceinline__ void load8(const bf16_t* p, float* v) {
+  const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(q[i] << 16);
+    v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_bf16_kernel(const bf16_t* __restrict__ y_perm,
+                                                           const bf16_t* __restrict__ y_shared,
+                                                           const int32_t* __restrict__ slot_of,
+                                                           const float* __restrict__ topk_w,
+                                                           bf16_t* __restrict__ out, int D, int k,
+                                                           int S, float alpha) {
+  __shared__ int slot_s[kMaxK];
+  __shared__ float coef_s[kMaxK];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    slot_s[threadIdx.x] = min(max(slot_of[static_cast<size_t>(t) * k + threadIdx.x], 0), S - 1);
+    coef_s[threadIdx.x] = alpha * topk_w[static_cast<size_t>(t) * k + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x * 8; c < D; c += blockDim.x * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      float v[8];
+      load8(y_perm + static_cast<size_t>(slot_s[j]) * D + c, v);
+      const float cj = coef_s[j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(cj, v[i], acc[i]);
+    }
+    if (y_shared) {
+      float v[8];
+      load8(y_shared + static_cast<size_t>(t) * D + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = v[i] + acc[i];
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(out + static_cast<size_t>(t) * D + c) = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restrict__ y_perm,
+                                                          const float* __restrict__ y_shared,
+                                                          const int32_t* __restrict__ slot_of,
+                                                          const float* __restrict__ topk_w,
+                                                          float* __restrict__ out, int D, int k,
+                                                          int S, float alpha) {
+  __shared__ int slot_s[kMaxK];
+  __shared__ float coef_s[kMaxK];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    slot_s[threadIdx.x] = min(max(slot_of[static_cast<size_t>(t) * k + threadIdx.x], 0), S - 1);
+    coef_s[threadIdx.x] = alpha * topk_w[static_cast<size_t>(t) * k + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x * 4; c < D; c += blockDim.x * 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(y_perm + static_cast<size_t>(slot_s[j]) * D + c);
+      const float cj = coef_s[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(cj, v[i], acc[i]);
+    }
+    if (y_shared) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(y_shared + static_cast<size_t>(t) * D + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = v[i] + acc[i];
+    }
+    *reinterpret_cast<f32x4*>(out + static_cast<size_t>(t) * D + c) = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_shared,
+                          const int32_t* slot_of, const float* topk_w, void* out,
+                          hipStream_t st) {
+  if (s.dtype == MOE_BF16)
+    combine_bf16_kernel<<<s.T, 256, 0, st>>>(static_cast<const bf16_t*>(y_perm),
+                                             static_cast<const bf16_t*>(y_shared), slot_of, topk_w,
+                                             static_cast<bf16_t*>(out), s.D, s.k, s.T * s.k, s.alpha);
+  else
+    combine_f32_kernel<<<s.T, 256, 0, st>>>(static_cast<const float*>(y_perm),
+                                            static_cast<const float*>(y_shared), slot_of, topk_w,
+                                            static_cast<float*>(out), s.D, s.k, s.T * s.k, s.alpha);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,69 @@
+// Internal declarations shared by the HIP translation units of libmoe.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- types
+typedef uint16_t bf16_t;   // bf16 bit pattern
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-a)); }
+
+// --------------------------------------------------------------- launchers
+// All return hipSuccess or the launch error; they assume validated arguments.
+hipError_t launch_route_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* wr,
+                             const float* bias, float* logits, int32_t* idx, float* w,
+                             hipStream_t st);
+hipError_t launch_route_f32(const moe_shape& s, const float* x, const float* wr,
+                            const float* bias, float* logits, int32_t* idx, float* w,
+                            hipStream_t st);
+
+size_t permute_workspace_bytes(const moe_shape& s);
+hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_token, int32_t* slot_of,
+                          void* x_perm, void* workspace, hipStream_t st);
+
+hipError_t launch_gate_up_bf16(const moe_shape& s, const bf16_t* x_perm,
+                               const int32_t* sorted_token, const bf16_t* x,
+                               const int32_t* offsets, const bf16_t* wgu, const bf16_t* wsgu,
+                               bf16_t* h, hipStream_t st);
+hipError_t launch_down_bf16(const moe_shape& s, const bf16_t* h, const int32_t* offsets,
+                            const bf16_t* wd, const bf16_t* wsd, bf16_t* y_perm,
+                            bf16_t* y_shared, hipStream_t st);
+hipError_t launch_gate_up_f32(const moe_shape& s, const float* x_perm,
+                              const int32_t* sorted_token, const float* x,
+                              const int32_t* offsets, const float* wgu, const float* wsgu,
+                              float* h, hipStream_t st);
+hipError_t launch_down_f32(const moe_shape& s, const float* h, const int32_t* offsets,
+                           const float* wd, const float* wsd, float* y_perm, float* y_shared,
+                           hipStream_t st);
+
+hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_shared,
+                          const int32_t* slot_of, const float* topk_w, void* out,
+                          hipStream_t st);
+
+}  // namespace moe

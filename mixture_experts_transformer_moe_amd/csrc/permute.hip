@@ -1,0 +1,175 @@
+// Expert-order permutation: the single-GPU form of the dispatch that the pages
+// fuse into their grouped GEMM ("copy expert tokens in expert order", "Laguna
+// M.1/XS.2 Technical Report", Key claims, report section 3.1.2, Fig. 2).
+//
+// Three index kernels and one copy, all deterministic (integer work only; LDS
+// atomics count and set bits, which gives the same result in any order):
+//   hist    one block per 256 tokens: per-block expert histogram -> workspace
+//   scan    one block: per-expert totals (counts), exclusive scan over experts
+//           (offsets), and for every block the first position of each expert's
+//           tokens in that block (written back over the histogram)
+//   scatter one block per 256 tokens: the rank of token t among the block's
+//           tokens of expert e is a popcount over an LDS bitmap of which tokens
+//           chose e; position = block base + rank, so each expert's tokens end
+//           up in ascending token order
+//   gather  x_perm[p] = x[sorted_token[p]] with 16-byte loads and stores,
+//           flattened over all (row, chunk) pairs
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTB = 256;        // tokens per block
+constexpr int kMaxE = 256;
+
+__device__ __forceinline__ int clamp_e(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+__global__ __launch_bounds__(kTB) void perm_hist_kernel(const int32_t* __restrict__ idx, int T,
+                                                        int E, int k, int32_t* __restrict__ blk) {
+  __shared__ int32_t hist[kMaxE];
+  for (int e = threadIdx.x; e < E; e += kTB) hist[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kTB + threadIdx.x;
+  if (t < T)
+    for (int j = 0; j < k; ++j) atomicAdd(&hist[clamp_e(idx[static_cast<size_t>(t) * k + j], E)], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kTB) blk[static_cast<size_t>(blockIdx.x) * E + e] = hist[e];
+}
+
+// 1024 threads: thread (part, e) sums a quarter of the blocks of expert e.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ blk, int nb, int E,
+                                                         int S, int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets) {
+  __shared__ int32_t part_sum[4][kMaxE];
+  __shared__ int32_t scan[kMaxE];
+  const int e = threadIdx.x & (kMaxE - 1);
+  const int part = threadIdx.x >> 8;
+  const int chunk = (nb + 3) / 4;
+  const int b_lo = part * chunk;
+  const int b_hi = min(nb, b_lo + chunk);
+  int sum = 0;
+  if (e < E)
+    for (int b = b_lo; b < b_hi; ++b) sum += blk[static_cast<size_t>(b) * E + e];
+  part_sum[part][e] = sum;
+  __syncthreads();
+  if (part == 0) {
+    const int c = e < E ? part_sum[0][e] + part_sum[1][e] + part_sum[2][e] + part_sum[3][e] : 0;
+    scan[e] = c;
+    if (e < E) counts[e] = c;
+  }
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the 256 expert totals
+  for (int off = 1; off < kMaxE; off <<= 1) {
+    int v = 0;
+    if (part == 0 && e >= off) v = scan[e - off];
+    __syncthreads();
+    if (part == 0) scan[e] += v;
+    __syncthreads();
+  }
+  const int excl_e = e == 0 ? 0 : scan[e - 1];
+  if (part == 0 && e < E) offsets[e] = excl_e;
+  if (threadIdx.x == 0) offsets[E] = S;
+  if (e < E) {
+    int base = excl_e;
+    for (int p = 0; p < part; ++p) base += part_sum[p][e];
+    for (int b = b_lo; b < b_hi; ++b) {
+      const size_t i = static_cast<size_t>(b) * E + e;
+      const int c = blk[i];
+      blk[i] = base;
+      base += c;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kTB) void perm_scatter_kernel(const int32_t* __restrict__ idx, int T,
+                                                           int E, int k,
+                                                           const int32_t* __restrict__ blk,
+                                                           int32_t* __restrict__ sorted_token,
+                                                           int32_t* __restrict__ slot_of) {
+  __shared__ uint32_t chose[kMaxE][kTB / 32];   // bit (t mod 256) of row e: token chose e
+  __shared__ int32_t base[kMaxE];
+  for (int i = threadIdx.x; i < kMaxE * (kTB / 32); i += kTB) (&chose[0][0])[i] = 0u;
+  for (int e = threadIdx.x; e < E; e += kTB) base[e] = blk[static_cast<size_t>(blockIdx.x) * E + e];
+  __syncthreads();
+  const int local = threadIdx.x;
+  const int t = blockIdx.x * kTB + local;
+  const int word = local >> 5;
+  const uint32_t bit = 1u << (local & 31);
+  if (t < T)
+    for (int j = 0; j < k; ++j)
+      atomicOr(&chose[clamp_e(idx[static_cast<size_t>(t) * k + j], E)][word], bit);
+  __syncthreads();
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = clamp_e(idx[static_cast<size_t>(t) * k + j], E);
+      int rank = __popc(chose[e][word] & (bit - 1u));
+      for (int w = 0; w < word; ++w) rank += __popc(chose[e][w]);
+      const int pos = base[e] + rank;
+      slot_of[static_cast<size_t>(t) * k + j] = pos;
+      sorted_token[pos] = t;
+    }
+  }
+}
+
+// Copies rows in 16-byte chunks; row_vec = chunks per row.
+__global__ __launch_bounds__(256) void perm_gather_kernel(const u32x4* __restrict__ x,
+                                                          const int32_t* __restrict__ sorted_token,
+                                                          u32x4* __restrict__ x_perm, int64_t total,
+                                                          int row_vec, int T) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; c + 3 * stride < total; c += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t cc = c + u * stride;
+      const int64_t p = cc / row_vec;
+      const int col = static_cast<int>(cc - p * row_vec);
+      const int t = min(max(sorted_token[p], 0), T - 1);
+      v[u] = x[static_cast<int64_t>(t) * row_vec + col];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x_perm[c + u * stride] = v[u];
+  }
+  for (; c < total; c += stride) {
+    const int64_t p = c / row_vec;
+    const int col = static_cast<int>(c - p * row_vec);
+    const int t = min(max(sorted_token[p], 0), T - 1);
+    x_perm[c] = x[static_cast<int64_t>(t) * row_vec + col];
+  }
+}
+
+}  // namespace
+
+size_t permute_workspace_bytes(const moe_shape& s) {
+  const size_t nb = (static_cast<size_t>(s.T) + kTB - 1) / kTB;
+  const size_t b = nb * static_cast<size_t>(s.E) * sizeof(int32_t);
+  return (b + 255) / 256 * 256;
+}
+
+hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_token, int32_t* slot_of,
+                          void* x_perm, void* workspace, hipStream_t st) {
+  const int nb = (s.T + kTB - 1) / kTB;
+  int32_t* blk = static_cast<int32_t*>(workspace);
+  const int S = s.T * s.k;
+  hipError_t err;
+  perm_hist_kernel<<<nb, kTB, 0, st>>>(idx, s.T, s.E, s.k, blk);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  perm_scan_kernel<<<1, 1024, 0, st>>>(blk, nb, s.E, S, counts, offsets);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  perm_scatter_kernel<<<nb, kTB, 0, st>>>(idx, s.T, s.E, s.k, blk, sorted_token, slot_of);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (x_perm) {
+    const int elem = s.dtype == MOE_BF16 ? 2 : 4;
+    const int row_vec = s.D * elem / 16;
+    const int64_t total = static_cast<int64_t>(S) * row_vec;
+    const int64_t want = (total + 256 * 4 - 1) / (256 * 4);
+    const int blocks = static_cast<int>(want < 16384 ? (want > 0 ? want : 1) : 16384);
+    perm_gather_kernel<<<blocks, 256, 0, st>>>(static_cast<const u32x4*>(x), sorted_token,
+                                               static_cast<u32x4*>(x_perm), total, row_vec, s.T);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -45,7 +45,7 @@ hand-derived single-channel values, and the parameter counts of the
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Callable, Dict, Iterable, Optional, Tuple
+from typing import Iterable, Optional, Tuple
 
 import numpy as np
 
@@ -163,23 +163,6 @@ def swiglu_expert(xrows: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray) 
     return (silu(g) * u) @ w_down.T
 
 
-class _WeightCache:
-    """Widens one expert's stored weights at a time (bounded memory)."""
-
-    def __init__(self, inputs, max_items: int = 16):
-        self.inputs = inputs
-        self.max_items = max_items
-        self._c: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
-
-    def routed(self, e: int):
-        if e not in self._c:
-            if len(self._c) >= self.max_items:
-                self._c.pop(next(iter(self._c)))
-            a, b = self.inputs.expert(e)
-            self._c[e] = (widen(a), widen(b))
-        return self._c[e]
-
-
 def shared_output(inputs, xrows64: np.ndarray) -> np.ndarray:
     sh = inputs.shared()
     if sh is None:
@@ -217,25 +200,26 @@ def forward(inputs, alpha: float, k: int, logits32: Optional[np.ndarray] = None)
     return out, r
 
 
-def forward_tokens(inputs, alpha: float, routing: Routing, tokens: Iterable[int],
-                   cache: Optional[_WeightCache] = None) -> np.ndarray:
-    """Output rows of the given tokens only, under a given routing (float64)."""
+def forward_tokens(inputs, alpha: float, routing: Routing, tokens: Iterable[int]) -> np.ndarray:
+    """Output rows of the given tokens only, under a given routing (float64).
+
+    Each expert used by these tokens is widened once and applied to the tokens
+    that selected it.
+    """
     tokens = np.asarray(list(tokens), dtype=np.int64)
-    cache = cache or _WeightCache(inputs)
     x = widen(np.asarray(inputs.x)[tokens])
     out = shared_output(inputs, x)
-    for i, t in enumerate(tokens):
-        acc = np.zeros(x.shape[1], dtype=np.float64)
-        for j in range(routing.topk_idx.shape[1]):
-            e = int(routing.topk_idx[t, j])
-            wgu, wd = cache.routed(e)
-            acc += routing.topk_w[t, j] * swiglu_expert(x[i:i + 1], wgu, wd)[0]
-        out[i] += alpha * acc
-    return out
+    routed = np.zeros_like(out)
+    sel = routing.topk_idx[tokens]
+    for e in np.unique(sel):
+        rows, slots = np.nonzero(sel == e)
+        a, b = inputs.expert(int(e))
+        y = swiglu_expert(x[rows], widen(a), widen(b))
+        routed[rows] += routing.topk_w[tokens[rows], slots][:, None] * y
+    return out + alpha * routed
 
 
-def expert_rows(inputs, routing: Routing, e: int, rows: Optional[np.ndarray] = None,
-                cache: Optional[_WeightCache] = None):
+def expert_rows(inputs, routing: Routing, e: int, rows: Optional[np.ndarray] = None):
     """Hidden activations h and outputs y of expert e for its rows in expert order.
 
     ``rows`` are positions inside expert e's segment (default: all).  Returns
@@ -243,8 +227,7 @@ def expert_rows(inputs, routing: Routing, e: int, rows: Optional[np.ndarray] = N
     """
     lo, hi = int(routing.offsets[e]), int(routing.offsets[e + 1])
     pos = np.arange(lo, hi) if rows is None else lo + np.asarray(rows, dtype=np.int64)
-    cache = cache or _WeightCache(inputs)
-    wgu, wd = cache.routed(e)
+    wgu, wd = (widen(a) for a in inputs.expert(e))
     xr = widen(np.asarray(inputs.x)[routing.sorted_token[pos]])
     F = wgu.shape[0] // 2
     h = silu(xr @ wgu[:F].T) * (xr @ wgu[F:].T)

@@ -1,0 +1,97 @@
+"""Shared GPU-test plumbing: run the layer through the C ABI and pull results
+back to the host; compare them with the CPU oracle."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+from mixture_experts_transformer_moe_amd import binding
+from mixture_experts_transformer_moe_amd.inputs import LayerInputs
+
+
+def say(msg: str) -> None:
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+class StackedInputs:
+    """Seeded inputs with the routed weights already stacked in host memory."""
+
+    def __init__(self, inputs: LayerInputs):
+        self.shape = inputs.shape
+        self.x = inputs.x
+        self.w_router = inputs.w_router
+        self.bias = inputs.bias
+        self.wgu, self.wd = inputs.all_experts()
+        self._shared = inputs.shared()
+
+    def expert(self, e):
+        return self.wgu[e], self.wd[e]
+
+    def shared(self):
+        return self._shared
+
+
+def upload_stacked(inp: StackedInputs, device="cuda"):
+    s = inp.shape
+    td = lambda a: binding.to_device(a, s, device)
+    w = binding.LayerWeights(
+        w_router=td(inp.w_router),
+        bias=None if inp.bias is None else torch.from_numpy(np.asarray(inp.bias, np.float32)).to(device),
+        w_gate_up=td(inp.wgu), w_down=td(inp.wd),
+        ws_gate_up=None if inp.shared() is None else td(inp.shared()[0]),
+        ws_down=None if inp.shared() is None else td(inp.shared()[1]))
+    return td(inp.x), w
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run_layer(s, inp: StackedInputs, gather: bool = False):
+    say(f"layer {s.name} T={s.T} D={s.D} E={s.E} k={s.k} F={s.F} Fs={s.Fs} gather={gather}")
+    x, w = upload_stacked(inp)
+    b = binding.alloc_buffers(s, with_x_perm=not gather)
+    binding.layer_forward(s, x, w, b)
+    torch.cuda.synchronize()
+    say("layer done")
+    return x, w, b
+
+
+def check_routing(s, inp, b, logit_rtol=1e-5):
+    """Logits within tolerance; routing and expert order bit-exact against the
+    oracle decided on the GPU's fp32 logits.  Returns the oracle routing."""
+    logits = b.logits.cpu().numpy()
+    z64 = O.router_logits(inp.x, inp.w_router, inp.bias)
+    err = np.abs(logits.astype(np.float64) - z64).max()
+    assert err <= logit_rtol * np.abs(z64).max(), f"logit error {err} vs max {np.abs(z64).max()}"
+    r = O.route_from_fp32_logits(logits, s.k)
+    g_idx = b.topk_idx.cpu().numpy()
+    assert np.array_equal(g_idx, r.topk_idx), "topk_idx differs"
+    np.testing.assert_allclose(b.topk_w.cpu().numpy(), r.topk_w, rtol=1e-6, atol=0)
+    assert np.array_equal(b.counts.cpu().numpy(), r.counts), "counts differ"
+    assert np.array_equal(b.offsets.cpu().numpy(), r.offsets), "offsets differ"
+    assert np.array_equal(b.sorted_token.cpu().numpy(), r.sorted_token), "sorted_token differs"
+    assert np.array_equal(b.slot_of.cpu().numpy(), r.slot_of), "slot_of differs"
+    O.check_invariants(g_idx, b.topk_w.cpu().numpy(), b.counts.cpu().numpy(), b.offsets.cpu().numpy(),
+                       b.sorted_token.cpu().numpy(), b.slot_of.cpu().numpy(), s.E, w_tol=1e-6)
+    # routing of the self-contained oracle (its own fp64 logits), for the record
+    r64 = O.route(z64, s.k)
+    n_diff = int(np.sum(np.any(np.sort(r64.topk_idx, 1) != np.sort(r.topk_idx, 1), axis=1)))
+    say(f"routing bit-exact; tokens whose fp64-logit routing differs: {n_diff}")
+    return r
+
+
+def out_tolerance(s) -> float:
+    return 1e-5 if s.dtype == "f32" else 2e-2
+
+
+def assert_close_rel(got, ref, rtol, what):
+    err = np.abs(got - ref).max()
+    scale = np.abs(ref).max()
+    assert err <= rtol * scale, f"{what}: max|gpu-oracle| = {err:.3e} > {rtol} * {scale:.3e}"
+    return err / scale if scale else 0.0

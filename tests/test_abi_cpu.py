@@ -1,0 +1,103 @@
+"""The C ABI library on the host (no GPU needed): it loads, exports every entry
+point include/moe.h declares, and rejects bad arguments before launching."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_transformer_moe_amd import binding, configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        from mixture_experts_transformer_moe_amd.build import build
+        build(verbose=False)
+    return binding.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.moe_version() == 1
+    for st in range(5):
+        assert L.moe_status_string(st)
+    assert L.moe_status_string(99) == b"unknown status"
+
+
+def _shape(**kw):
+    s = configs.variant(configs.XS2_T4096, **kw) if kw else configs.XS2_T4096
+    return binding.make_shape(s)
+
+
+def _route(L, shape, ptr=16 * 1024):
+    p = ctypes.c_void_p(ptr)
+    return L.moe_route(ctypes.byref(shape), p, p, None, p, p, p, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), binding.MOE_ERR_INVALID_ARG),
+    (dict(k=300, E=256), binding.MOE_ERR_INVALID_ARG),
+    (dict(E=0), binding.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), binding.MOE_ERR_INVALID_ARG),
+    (dict(alpha=float("nan")), binding.MOE_ERR_INVALID_ARG),
+    (dict(E=512), binding.MOE_ERR_UNSUPPORTED),
+    (dict(k=17, E=64), binding.MOE_ERR_UNSUPPORTED),
+    (dict(D=2000), binding.MOE_ERR_UNSUPPORTED),
+    (dict(F=500), binding.MOE_ERR_UNSUPPORTED),
+    (dict(Fs=100), binding.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 28), binding.MOE_ERR_UNSUPPORTED),
+])
+def test_bad_shapes_are_rejected_before_launch(L, kw, status):
+    assert _route(L, _shape(**kw)) == status
+    assert L.moe_last_error()
+    assert L.moe_workspace_bytes(ctypes.byref(_shape(**kw))) == 0
+
+
+def test_bad_pointers_are_rejected(L):
+    s = _shape()
+    p = ctypes.c_void_p(4096)
+    assert L.moe_route(ctypes.byref(s), None, p, None, p, p, p, None) == binding.MOE_ERR_INVALID_ARG
+    assert b"x is NULL" in L.moe_last_error()
+    assert L.moe_route(ctypes.byref(s), ctypes.c_void_p(4098), p, None, p, p, p, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    assert b"aligned" in L.moe_last_error()
+    assert L.moe_route(None, p, p, None, p, p, p, None) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(ctypes.byref(s), p, None, p, None, p, None) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_ffn(ctypes.byref(s), None, None, p, p, p, p, p, p, p, p, p, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    assert b"sorted_token" in L.moe_last_error()
+
+
+def test_workspace_checks(L):
+    s = _shape()
+    need = L.moe_workspace_bytes(ctypes.byref(s))
+    assert need >= 16 * 256 * 4 and need % 256 == 0      # one histogram row per 256 tokens
+    p = ctypes.c_void_p(4096)
+    st = L.moe_permute(ctypes.byref(s), p, p, p, p, p, p, None, p, need - 1, None)
+    assert st == binding.MOE_ERR_WORKSPACE
+    st = L.moe_permute(ctypes.byref(s), p, p, p, p, p, p, None, None, need, None)
+    assert st == binding.MOE_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_no_op(L):
+    s = _shape(T=0)
+    assert _route(L, s, ptr=0) == binding.MOE_OK
+    assert L.moe_combine(ctypes.byref(s), None, None, None, None, None, None) == binding.MOE_OK

@@ -1,0 +1,194 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Routing and the expert order must be bit-exact (oracle decided on the GPU's
+fp32 logits); outputs within 2e-2 * max|oracle| for bf16 and 1e-5 * max|oracle|
+for fp32.  Small shapes compare every output element; the full-size workloads
+compare sampled tokens (the oracle evaluates them one by one) plus sampled rows
+of the intermediate h and y_perm.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from mixture_experts_transformer_moe_amd import binding, configs
+from mixture_experts_transformer_moe_amd.inputs import LayerInputs
+from tests.gpu_common import (StackedInputs, assert_close_rel, check_routing, out_tolerance,
+                              run_layer, say, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = configs.variant(configs.XS2_T4096, name="small_bf16_t300", T=300, D=256, E=16, k=4,
+                             F=128, Fs=128)
+
+
+def full_parity(s, inp=None, gather=False):
+    inp = inp or StackedInputs(LayerInputs(s))
+    x, w, b = run_layer(s, inp, gather=gather)
+    r = check_routing(s, inp, b)
+    ref, _ = O.forward(inp, s.alpha, s.k, logits32=b.logits.cpu().numpy())
+    rel = assert_close_rel(to_f64(b.out), ref, out_tolerance(s), "out")
+    say(f"{s.name}: out max rel err {rel:.2e}")
+    return inp, b, r
+
+
+def sampled_parity(s, n_tokens=40, seed=0):
+    inp = StackedInputs(LayerInputs(s))
+    x, w, b = run_layer(s, inp)
+    r = check_routing(s, inp, b)
+    rng = np.random.default_rng(seed)
+    toks = set(rng.choice(s.T, size=min(n_tokens, s.T), replace=False).tolist()) | {0, s.T - 1}
+    busiest = int(np.argmax(r.counts))
+    toks |= set(r.sorted_token[r.offsets[busiest]:r.offsets[busiest] + 4].tolist())
+    if s.outlier_frac > 0:
+        from mixture_experts_transformer_moe_amd.inputs import outlier_tokens
+        toks |= set(outlier_tokens(s)[:6].tolist())
+    toks = sorted(toks)
+    say(f"oracle on {len(toks)} sampled tokens")
+    ref = O.forward_tokens(inp, s.alpha, r, toks)
+    rel = assert_close_rel(to_f64(b.out[toks]), ref, out_tolerance(s), "sampled out")
+    say(f"{s.name}: sampled out max rel err {rel:.2e}")
+    # intermediate rows of a few experts: busiest, smallest non-empty, a random one
+    nz = np.nonzero(r.counts)[0]
+    experts = {busiest, int(nz[np.argmin(r.counts[nz])]), int(rng.choice(nz))}
+    h = b.h[: s.S * s.F].view(s.S, s.F)
+    for e in sorted(experts):
+        n = int(r.counts[e])
+        rows = np.unique(np.array([0, n - 1, n // 2]))
+        h_ref, y_ref = O.expert_rows(inp, r, e, rows)
+        pos = int(r.offsets[e]) + rows
+        assert_close_rel(to_f64(h[pos]), h_ref, out_tolerance(s), f"h of expert {e}")
+        assert_close_rel(to_f64(b.y_perm[pos]), y_ref, out_tolerance(s), f"y_perm of expert {e}")
+    return inp, b, r
+
+
+# ------------------------------------------------------------------ workloads
+
+def test_tiny_f32_full_parity():
+    full_parity(configs.TINY_F32)
+
+
+def test_small_bf16_full_parity_ragged():
+    full_parity(SMALL_BF16)
+
+
+def test_small_bf16_gather_mode_matches_x_perm_mode():
+    s = SMALL_BF16
+    inp = StackedInputs(LayerInputs(s))
+    _, _, b1 = run_layer(s, inp, gather=False)
+    _, _, b2 = run_layer(s, inp, gather=True)
+    assert torch.equal(b1.out, b2.out)
+    assert torch.equal(b1.h, b2.h)
+
+
+@pytest.mark.parametrize("name", [configs.XS2_T4096.name, configs.M1_T8192.name,
+                                  configs.DECODE_SKEW_T32.name,
+                                  configs.PREFILL_OUTLIER_T32768.name])
+def test_full_size_workload_sampled_parity(name):
+    sampled_parity(configs.get(name))
+
+
+def test_decode_workload_full_parity():
+    # T = 32: the oracle evaluates the whole layer
+    inp, b, r = full_parity(configs.DECODE_SKEW_T32)
+    say(f"decode: experts touched {int(np.count_nonzero(r.counts))}, max rows {int(r.counts.max())}")
+
+
+# ------------------------------------------------------------------ edge cases
+
+EDGE = {
+    "k1": dict(k=1),
+    "k_eq_E": dict(E=16, k=16),
+    "E1_k1": dict(E=1, k=1),
+    "no_shared": dict(Fs=0),
+    "T1": dict(T=1),
+    "T33_wide_shared": dict(T=33, Fs=256),
+    "E256_T70": dict(T=70, E=256, k=8),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_edge_shapes_bf16(case):
+    s = configs.variant(SMALL_BF16, name=f"edge_{case}", **EDGE[case])
+    full_parity(s)
+
+
+@pytest.mark.parametrize("case", ["k1", "no_shared", "T1", "k_eq_E"])
+def test_edge_shapes_f32(case):
+    s = configs.variant(configs.TINY_F32, name=f"edge_f32_{case}", **EDGE[case])
+    full_parity(s)
+
+
+def test_zero_router_ties_go_to_lowest_indices():
+    s = configs.variant(SMALL_BF16, name="zero_router", T=100)
+    inp = StackedInputs(LayerInputs(s))
+    inp.w_router = np.zeros_like(inp.w_router)
+    _, b, r = full_parity(s, inp)
+    assert (b.topk_idx.cpu().numpy() == np.arange(s.k)).all()
+    np.testing.assert_allclose(b.topk_w.cpu().numpy(), 1.0 / s.k, rtol=1e-6)
+
+
+def test_one_expert_takes_every_token():
+    s = configs.variant(SMALL_BF16, name="hot_expert", T=520)
+    bias = np.zeros(s.E, np.float32)
+    bias[3] = 30.0
+    inp = StackedInputs(LayerInputs(s, bias=bias))
+    _, b, r = full_parity(s, inp)
+    assert int(b.counts[3]) == s.T
+
+
+def _guarded_like(t: torch.Tensor, pad: int = 4096):
+    """A buffer with t's shape followed by a guard region of known bytes."""
+    big = torch.empty(t.numel() + pad, dtype=t.dtype, device=t.device)
+    ints = big.view(torch.int16 if t.element_size() == 2 else torch.int32)
+    ints[t.numel():] = 0x5a5a if t.element_size() == 2 else 0x5a5a5a5a
+    return big, big[: t.numel()].view(t.shape)
+
+
+def _guard_intact(big: torch.Tensor, n: int) -> bool:
+    ints = big.view(torch.int16 if big.element_size() == 2 else torch.int32)[n:]
+    return bool((ints == (0x5a5a if big.element_size() == 2 else 0x5a5a5a5a)).all())
+
+
+def test_determinism_and_no_out_of_bounds_writes():
+    s = SMALL_BF16
+    inp = StackedInputs(LayerInputs(s))
+    from tests.gpu_common import upload_stacked
+    x, w = upload_stacked(inp)
+    outs = []
+    for rep in range(3):
+        say(f"determinism rep {rep}")
+        b = binding.alloc_buffers(s)
+        guards = {}
+        for name in ("logits", "topk_idx", "topk_w", "counts", "offsets", "sorted_token",
+                     "slot_of", "x_perm", "h", "y_perm", "y_shared", "out"):
+            t = getattr(b, name)
+            big, view = _guarded_like(t)
+            guards[name] = (big, t.numel())
+            setattr(b, name, view)
+        binding.layer_forward(s, x, w, b)
+        torch.cuda.synchronize()
+        for name, (big, n) in guards.items():
+            assert _guard_intact(big, n), f"write past the end of {name}"
+        outs.append((b.out.clone(), b.sorted_token.clone(), b.h.clone(), b.logits.clone()))
+    for o in outs[1:]:
+        assert all(torch.equal(p, q) for p, q in zip(o, outs[0]))
+
+
+def test_empty_batch_is_a_no_op():
+    s = configs.variant(SMALL_BF16, T=0)
+    c = binding.make_shape(s)
+    binding.moe_combine(c, None, None, None, None, None)
+    binding.moe_route(c, None, None, None, None, None, None)
+
+
+def test_invalid_arguments_raise_without_launch():
+    s = SMALL_BF16
+    b = binding.alloc_buffers(s)
+    c = binding.make_shape(configs.variant(s, k=0))
+    with pytest.raises(binding.MoEError):
+        binding.moe_combine(c, b.y_perm, b.y_shared, b.slot_of, b.topk_w, b.out)
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(binding.MoEError):
+        binding.moe_permute(binding.make_shape(s), b.topk_idx, b.out, b.counts, b.offsets,
+                            b.sorted_token, b.slot_of, None, small_ws)
