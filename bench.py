@@ -102,8 +102,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=configs.BENCH_WORKLOAD, choices=sorted(configs.WORKLOADS))
-    ap.add_argument("--gather", action="store_true",
-                    help="read A rows of the first GEMM through sorted_token instead of x_perm")
+    ap.add_argument("--x-perm", action="store_true",
+                    help="materialise x_perm in moe_permute and read it in the first GEMM "
+                         "(default: the first GEMM gathers token rows through sorted_token)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -130,7 +131,7 @@ def main():
         ws_gate_up=None if host["shared"] is None else td(host["shared"][0]),
         ws_down=None if host["shared"] is None else td(host["shared"][1]))
     x = td(inp.x)
-    b = binding.alloc_buffers(s, dev, with_x_perm=not args.gather)
+    b = binding.alloc_buffers(s, dev, with_x_perm=args.x_perm)
     c = binding.make_shape(s)
     stream = torch.cuda.current_stream(dev)
 
@@ -194,7 +195,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": s.name, "tokens": s.T, "d_model": s.D, "experts": s.E,
                    "top_k": s.k, "expert_width": s.F, "shared_width": s.Fs, "alpha": s.alpha,
-                   "a_rows": "gather" if args.gather else "x_perm", "parallelism": "single-gpu"},
+                   "a_rows": "x_perm" if args.x_perm else "gather", "parallelism": "single-gpu"},
         "layer_tflops": round(layer_tflops, 1),
         "experts_touched": n_touched, "rows_per_expert_max": int(counts.max()),
         "roofline": roof, "cpu_baseline": cpu,

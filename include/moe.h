@@ -36,7 +36,7 @@
  *
  * Shape limits (else MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED):
  *   1 <= E <= 256, 1 <= k <= min(E, 16), T >= 0, T * k < 2^31.
- *   MOE_BF16: D % 128 == 0, F % 64 == 0, Fs % 64 == 0 (Fs == 0 = no shared expert).
+ *   MOE_BF16: D % 256 == 0, F % 128 == 0, Fs % 128 == 0 (Fs == 0 = no shared expert).
  *   MOE_F32:  D % 4 == 0, F % 4 == 0, Fs % 4 == 0.
  */
 #ifndef MOE_H_

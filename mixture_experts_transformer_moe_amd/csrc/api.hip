@@ -54,9 +54,9 @@ int check_shape(const moe_shape* s) {
   if (static_cast<int64_t>(s->T) * s->k >= (int64_t{1} << 31))
     return fail(MOE_ERR_UNSUPPORTED, "k*T = %lld does not fit int32", static_cast<long long>(s->T) * s->k);
   if (s->dtype == MOE_BF16) {
-    if (s->D % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: D = %d is not a multiple of 128", s->D);
-    if (s->F % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: F = %d is not a multiple of 64", s->F);
-    if (s->Fs % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: Fs = %d is not a multiple of 64", s->Fs);
+    if (s->D % 256 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: D = %d is not a multiple of 256", s->D);
+    if (s->F % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: F = %d is not a multiple of 128", s->F);
+    if (s->Fs % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: Fs = %d is not a multiple of 128", s->Fs);
   } else {
     if (s->D % 4 != 0 || s->F % 4 != 0 || s->Fs % 4 != 0)
       return fail(MOE_ERR_UNSUPPORTED, "fp32: D, F and Fs must be multiples of 4");

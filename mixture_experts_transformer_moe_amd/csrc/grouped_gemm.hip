@@ -16,22 +16,19 @@
 //     tile range is cut into 8 contiguous chunks, one per XCD (workgroup b runs
 //     on XCD b % 8), so the workgroups that share a weight tile run at the
 //     same time behind the same L2;
-//   * 128 x 128 x 64 block tile, 4 waves of 64 x 64, v_mfma_f32_32x32x16_bf16,
-//     double-buffered LDS with an XOR swizzle of the 16-byte chunks (conflict-
-//     free ds_read_b128), global loads for step k+1 in flight during step k;
-//   * gate_up: the 128 B-rows of a tile are 64 gate rows and the 64 matching up
-//     rows, and every wave holds a gate block and the up block of the same
-//     columns, so SwiGLU is applied in registers before one rounding to bf16;
+//   * BM x 256 tiles (BM by the mean rows per expert), one workgroup per CU,
+//     both operands streamed by direct global->LDS loads through a ring of
+//     stages (mma_pipeline.h); gate_up tiles pair each gate block with the up
+//     block of the same columns, so SwiGLU is applied in registers before one
+//     rounding to bf16;
 //   * epilogue staged through LDS for 16-byte coalesced row stores.
-#include "moe_internal.h"
+#include "mma_pipeline.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 128;           // B rows per tile
-constexpr int BK = 64;
-constexpr int kThreads = 256;
+constexpr int BK = kPipeBK;
+constexpr int kThreads = kPipeThreads;
 constexpr int kMaxE = 256;
 constexpr int kXcds = 8;
 
@@ -52,13 +49,19 @@ struct GemmArgs {
   int has_shared;
 };
 
-// element offset of 16-byte chunk `ch` of row `row` in a [rows][64] bf16 tile
-__device__ __forceinline__ int swz(int row, int ch) { return row * BK + ((ch ^ (row & 7)) << 3); }
-
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs g) {
-  constexpr int kOutCols = (MODE == kGateUp) ? BN / 2 : BN;   // output columns per tile
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][(BM + BN) * BK];
+// One kernel for both GEMMs: a tile is BM rows of one group x 256 weight rows
+// (gate_up: 128 gate rows and the 128 up rows of the same columns; down: 256
+// output columns); the four waves split the weight rows, 64 each, and run the
+// shared pipeline (mma_pipeline.h).
+template <int MODE, int BM, int NS>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
+  using PS = PipeShape<BM, NS>;
+  constexpr int MB = BM / 32;                                   // 32-row MFMA blocks per wave
+  constexpr int kOutCols = (MODE == kGateUp) ? 128 : 256;       // output columns per tile
+  constexpr int kStageLd = kOutCols + 8;                        // padded epilogue row
+  constexpr int kHalfRows = BM * kStageLd > PS::kStageElems ? BM / 2 : BM;   // epilogue pass height
+  static_assert(kHalfRows * kStageLd <= PS::kStageElems, "epilogue staging");
+  __shared__ __attribute__((aligned(16))) bf16_t lds[PS::kLdsElems];
   __shared__ int tile_end[kMaxE + 1];
   __shared__ int row_base[kMaxE + 1];
 
@@ -105,7 +108,6 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs g) {
 
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
 
   for (int ti = t_lo + slot; ti < t_hi; ti += per_xcd) {
     // group of this tile: first g with tile_end[g] > ti
@@ -124,15 +126,15 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs g) {
     const int n_tile = local / mt;
     const int K = shared ? g.Ks : g.K;
     const int Nout = shared ? g.Ns : g.N;
-    const int KT = K / BK;
+    const int NKB = K / BK;
+    const int mb_valid = min(MB, (M - m0 + 31) >> 5);
 
-    // ---- per-thread source rows for the A and B tiles (4 chunks each)
-    const bf16_t* a_ptr[4];
-    const bf16_t* b_ptr[4];
+    // ---- DMA sources of this lane (see dma_chunk): A rows, then B rows
+    const bf16_t* a_src[PS::kAInst];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = tid + kThreads * q;
-      const int row = c >> 3, ch = c & 7;
+    for (int q = 0; q < PS::kAInst; ++q) {
+      int row, col;
+      dma_chunk<PS::kAInst>(q, row, col);
       const int r = min(m0 + row, M - 1);                // rows past M are computed and dropped
       const bf16_t* arow;
       if (shared) {
@@ -143,114 +145,70 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs g) {
       } else {
         arow = g.a_routed + static_cast<size_t>(row_base[grp] + r) * K;
       }
-      a_ptr[q] = arow + ch * 8;
+      a_src[q] = arow + col;
+    }
+    const bf16_t* wbase = shared ? g.w_shared
+                                 : g.w_routed + static_cast<size_t>(grp) * (MODE == kGateUp ? 2 * Nout : Nout) * K;
+    const bf16_t* b_src[PS::kBInst];
+#pragma unroll
+    for (int q = 0; q < PS::kBInst; ++q) {
+      int row, col;
+      dma_chunk<PS::kBInst>(q, row, col);
       int wrow;
-      if (MODE == kGateUp) {
-        const int n0 = n_tile * kOutCols;
-        wrow = row < kOutCols ? n0 + row : Nout + n0 + (row - kOutCols);
-      } else {
-        wrow = n_tile * BN + row;
-      }
-      const bf16_t* wbase = shared ? g.w_shared
-                                   : g.w_routed + static_cast<size_t>(grp) * (MODE == kGateUp ? 2 * Nout : Nout) * K;
-      b_ptr[q] = wbase + static_cast<size_t>(wrow) * K + ch * 8;
+      if (MODE == kGateUp)   // B rows 0..127: gate rows; 128..255: the up rows of the same columns
+        wrow = (row < 128 ? 0 : Nout - 128) + n_tile * kOutCols + row;
+      else
+        wrow = n_tile * kOutCols + row;
+      b_src[q] = wbase + static_cast<size_t>(wrow) * K + col;
+    }
+    // this wave's two 32-row B blocks inside the tile
+    int brow[2];
+    if (MODE == kGateUp) {
+      brow[0] = 32 * wave;
+      brow[1] = 128 + 32 * wave;
+    } else {
+      brow[0] = 64 * wave;
+      brow[1] = 64 * wave + 32;
     }
 
-    u32x4 ra[4], rb[4];
-    auto gload = [&](int k0) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        ra[q] = *reinterpret_cast<const u32x4*>(a_ptr[q] + k0);
-        rb[q] = *reinterpret_cast<const u32x4*>(b_ptr[q] + k0);
-      }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = tid + kThreads * q;
-        const int row = c >> 3, ch = c & 7;
-        *reinterpret_cast<u32x4*>(&lds[buf][swz(row, ch)]) = ra[q];
-        *reinterpret_cast<u32x4*>(&lds[buf][BM * BK + swz(row, ch)]) = rb[q];
-      }
-    };
+    f32x16 acc[MB][2];
+    mma_pipeline<BM, NS>(a_src, b_src, NKB, mb_valid, brow, lds, acc);
 
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{0.f};
-
-    // rows of this wave's MFMA blocks inside the tile
-    int arow_blk[2], brow_blk[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) arow_blk[i] = 64 * wm + 32 * i + (lane & 31);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      brow_blk[j] = (MODE == kGateUp ? 64 * j + 32 * wn : 64 * wn + 32 * j) + (lane & 31);
-    const int khalf = lane >> 5;
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < KT) gload((kt + 1) * BK);
-      const bf16_t* As = &lds[buf][0];
-      const bf16_t* Bs = &lds[buf][BM * BK];
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int ch = 2 * kk + khalf;
-        bf16x8 af[2], bfr[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&As[swz(arow_blk[i], ch)]));
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&Bs[swz(brow_blk[j], ch)]));
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-      if (kt + 1 < KT) sstore(buf ^ 1);
-      __syncthreads();
-    }
-
-    // ---- epilogue: registers -> LDS tile (bf16) -> 16-byte row stores
-    bf16_t* stage = &lds[0][0];
-    constexpr int kStageLd = kOutCols + 8;           // padded row (bf16 elements)
-    // C layout: lane holds column (lane & 31), register r -> row (r/4)*8 + (lane/32)*4 + r%4
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 64 * wm + 32 * i + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (MODE == kGateUp) {
-          const int col = 32 * wn + (lane & 31);
-          const float gv = acc[i][0][r], uv = acc[i][1][r];
-          stage[row * kStageLd + col] = f32_to_bf16(gv / (1.0f + __expf(-gv)) * uv);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = 64 * wn + 32 * j + (lane & 31);
-            stage[row * kStageLd + col] = f32_to_bf16(acc[i][j][r]);
-          }
-        }
-      }
-    }
-    __syncthreads();
+    // ---- epilogue: registers -> LDS tile (bf16) -> 16-byte row stores, in
+    // passes of kHalfRows rows through the start of the LDS ring
     constexpr int kChunksPerRow = kOutCols / 8;
     bf16_t* out = shared ? g.out_shared : g.out_routed + static_cast<size_t>(row_base[grp]) * Nout;
     const int n0 = n_tile * kOutCols;
-    for (int c = tid; c < BM * kChunksPerRow; c += kThreads) {
-      const int row = c / kChunksPerRow, ch = c % kChunksPerRow;
-      if (m0 + row < M) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[row * kStageLd + ch * 8]);
-        *reinterpret_cast<u32x4*>(out + static_cast<size_t>(m0 + row) * Nout + n0 + ch * 8) = v;
+#pragma unroll
+    for (int pass = 0; pass < BM / kHalfRows; ++pass) {
+#pragma unroll
+      for (int m = pass * (kHalfRows / 32); m < (pass + 1) * (kHalfRows / 32); ++m) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * m + mfma32_row(r, lane) - pass * kHalfRows;
+          if (MODE == kGateUp) {
+            const int col = 32 * wave + (lane & 31);
+            const float gv = acc[m][0][r], uv = acc[m][1][r];
+            lds[row * kStageLd + col] = f32_to_bf16(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int col = 64 * wave + 32 * j + (lane & 31);
+              lds[row * kStageLd + col] = f32_to_bf16(acc[m][j][r]);
+            }
+          }
+        }
       }
+      __syncthreads();
+      const int rows = min(kHalfRows, M - m0 - pass * kHalfRows);
+      for (int c = tid; c < rows * kChunksPerRow; c += kThreads) {
+        const int row = c / kChunksPerRow, ch = c % kChunksPerRow;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&lds[row * kStageLd + ch * 8]);
+        *reinterpret_cast<u32x4*>(out + static_cast<size_t>(m0 + pass * kHalfRows + row) * Nout + n0 +
+                                  ch * 8) = v;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
@@ -263,9 +221,23 @@ int persistent_grid() {
       if (hipGetDeviceProperties(&p, dev) == hipSuccess && p.multiProcessorCount > 0)
         cus = p.multiProcessorCount;
     }
-    grid = ((cus * 2 + kXcds - 1) / kXcds) * kXcds;   // two workgroups per CU
+    grid = ((cus + kXcds - 1) / kXcds) * kXcds;   // one workgroup per CU
   }
   return grid;
+}
+
+// Row-block height by the mean rows per expert (k*T/E): tall tiles when experts
+// hold many rows (fewer weight re-reads), short ones for decode-sized batches.
+template <int MODE>
+hipError_t launch_tiles(const GemmArgs& a, const moe_shape& s, hipStream_t st) {
+  const int mean_rows = (s.T * s.k) / s.E;
+  if (mean_rows >= 96)
+    grouped_gemm_kernel<MODE, 128, 3><<<persistent_grid(), kThreads, 0, st>>>(a);
+  else if (mean_rows >= 48)
+    grouped_gemm_kernel<MODE, 64, 3><<<persistent_grid(), kThreads, 0, st>>>(a);
+  else
+    grouped_gemm_kernel<MODE, 32, 4><<<persistent_grid(), kThreads, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -291,8 +263,7 @@ hipError_t launch_gate_up_bf16(const moe_shape& s, const bf16_t* x_perm,
   a.N = s.F;
   a.Ns = s.Fs;
   a.has_shared = s.Fs > 0;
-  grouped_gemm_kernel<kGateUp><<<persistent_grid(), kThreads, 0, st>>>(a);
-  return hipGetLastError();
+  return launch_tiles<kGateUp>(a, s, st);
 }
 
 hipError_t launch_down_bf16(const moe_shape& s, const bf16_t* h, const int32_t* offsets,
@@ -315,8 +286,7 @@ hipError_t launch_down_bf16(const moe_shape& s, const bf16_t* h, const int32_t* 
   a.N = s.D;
   a.Ns = s.D;
   a.has_shared = s.Fs > 0;
-  grouped_gemm_kernel<kDown><<<persistent_grid(), kThreads, 0, st>>>(a);
-  return hipGetLastError();
+  return launch_tiles<kDown>(a, s, st);
 }
 
 }  // namespace moe

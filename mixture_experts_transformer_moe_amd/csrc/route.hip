@@ -4,16 +4,16 @@
 //
 // bf16 path: one workgroup of 4 waves per 32 tokens.  Wave w owns experts
 // [64w, 64w+64) and accumulates the 32 x 64 logit block with
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulation), reading its operand fragments
-// straight from global memory (the router weight, E x D, stays hot in L2).  The
-// bias is added once, the fp32 logits are stored, and the same values are
-// staged in LDS for the selection.
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulation) in the shared pipelined loop
+// (mma_pipeline.h): token rows and router-weight rows (hot in L2) stream into
+// LDS through a ring of direct global->LDS loads.  The bias is added once,
+// the fp32 logits are stored, and the same values are staged in LDS for the
+// selection.
 //
-// Selection: one wave per token.  Each lane holds up to four candidates
-// (e = lane + 64 i) as 64-bit keys that order (z descending, e ascending), with
-// -0.0 folded onto +0.0.  k rounds of a wave-wide max pick the slots in order,
-// so the result is exact and does not depend on timing.
-#include "moe_internal.h"
+// Selection: one wave per token, k rounds of a DPP wave maximum over an
+// order-preserving uint32 image of the logits, ties resolved to the lower
+// expert index by ballots; exact and independent of timing.
+#include "mma_pipeline.h"
 
 namespace moe {
 namespace {
@@ -21,45 +21,59 @@ namespace {
 constexpr int kRouteTokens = 32;
 constexpr int kMaxE = 256;
 
-__device__ __forceinline__ uint64_t order_key(float z, int e) {
+// Monotone map of fp32 onto uint32 (larger z -> larger key); -0.0 is folded
+// onto +0.0 first so that the two zeros tie.
+__device__ __forceinline__ uint32_t order_key(float z) {
   uint32_t u = __float_as_uint(z);
-  if (u == 0x80000000u) u = 0u;                          // -0.0 == +0.0
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);        // monotone in z
-  // low half: larger for lower expert index; always >= 0xFF00, so a valid key
-  // is never 0 (0 marks "taken / absent").
-  return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(0xFFFFu - e);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
+// Maximum of v over the wave: DPP shifts inside each row of 16 lanes, then the
+// four row maxima through readlane.  The result is wave-uniform.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
+  return max(max(r0, r1), max(r2, r3));
 }
 
 // One wave selects the top-k of zrow[0..E) and writes slot order + weights.
+// Lane l holds candidates e = l + 64 i (i < 4).  Each round takes the largest
+// key among the candidates not yet taken (wave max), then the lowest index
+// holding it (ballots scanned in index order), so the order is (z descending,
+// index ascending) exactly, whatever the values (non-finite ones included).
 __device__ void wave_topk(const float* zrow, int E, int k, int32_t* idx_out, float* w_out) {
   const int lane = threadIdx.x & 63;
-  uint64_t key[4];
+  uint32_t key[4];
+  uint32_t taken = 0;                       // bit i: candidate i taken or absent
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    key[i] = e < E ? order_key(zrow[e], e) : 0ull;
+    key[i] = e < E ? order_key(zrow[e]) : 0u;
+    if (e >= E) taken |= 1u << i;
   }
   int my_e = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    uint32_t m = 0;
 #pragma unroll
-    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = 0xFFFF - static_cast<int>(best & 0xFFFFull);
-    if ((e & 63) == lane) {
+    for (int i = 0; i < 4; ++i)
+      if (!((taken >> i) & 1u)) m = max(m, key[i]);
+    const uint32_t best = wave_max_u32(m);
+    int e = 0;
+    bool found = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i == (e >> 6)) key[i] = 0ull;
+    for (int i = 0; i < 4; ++i) {
+      const unsigned long long b = __ballot(!((taken >> i) & 1u) && key[i] == best);
+      if (!found && b != 0ull) {
+        e = 64 * i + __ffsll(b) - 1;
+        found = true;
+      }
     }
+    if ((e & 63) == lane) taken |= 1u << (e >> 6);
     if (lane == j) my_e = e;
   }
   float s = 0.f;
@@ -72,50 +86,53 @@ __device__ void wave_topk(const float* zrow, int E, int k, int32_t* idx_out, flo
   }
 }
 
-__global__ __launch_bounds__(256) void route_bf16_kernel(const bf16_t* __restrict__ x,
-                                                         const bf16_t* __restrict__ wr,
-                                                         const float* __restrict__ bias,
-                                                         float* __restrict__ logits,
-                                                         int32_t* __restrict__ idx,
-                                                         float* __restrict__ wout, int T, int D,
-                                                         int E, int k) {
-  __shared__ float zs[kRouteTokens][kMaxE + 1];
+template <int NS>
+__global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __restrict__ x,
+                                                            const bf16_t* __restrict__ wr,
+                                                            const float* __restrict__ bias,
+                                                            float* __restrict__ logits,
+                                                            int32_t* __restrict__ idx,
+                                                            float* __restrict__ wout, int T, int D,
+                                                            int E, int k) {
+  using PS = PipeShape<kRouteTokens, NS>;
+  static_assert(kRouteTokens * (kMaxE + 1) * 2 <= PS::kLdsElems, "logit tile fits the ring");
+  __shared__ __attribute__((aligned(16))) bf16_t lds[PS::kLdsElems];
   const int t0 = blockIdx.x * kRouteTokens;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int e_base = 64 * wave;
 
-  if (e_base < E) {
-    f32x16 acc0 = {0.f}, acc1 = {0.f};
-    const int koff = (lane >> 5) * 8;
-    const int arow = min(t0 + (lane & 31), T - 1);
-    const int brow0 = min(e_base + (lane & 31), E - 1);
-    const int brow1 = min(e_base + 32 + (lane & 31), E - 1);
-    const bf16_t* pa = x + static_cast<size_t>(arow) * D + koff;
-    const bf16_t* pb0 = wr + static_cast<size_t>(brow0) * D + koff;
-    const bf16_t* pb1 = wr + static_cast<size_t>(brow1) * D + koff;
-    for (int k0 = 0; k0 < D; k0 += 16) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(pa + k0);
-      const u32x4 b0 = *reinterpret_cast<const u32x4*>(pb0 + k0);
-      const u32x4 b1 = *reinterpret_cast<const u32x4*>(pb1 + k0);
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, b0), acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, b1), acc1, 0, 0, 0);
-    }
-    // C layout of the 32x32 MFMA: lane holds column (lane & 31), register i holds
-    // row (i / 4) * 8 + (lane / 32) * 4 + (i % 4).
+  const bf16_t* a_src[PS::kAInst];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int col = e_base + 32 * nb + (lane & 31);
-      if (col < E) {
-        const float b = bias ? bias[col] : 0.f;
+  for (int q = 0; q < PS::kAInst; ++q) {
+    int row, col;
+    dma_chunk<PS::kAInst>(q, row, col);
+    a_src[q] = x + static_cast<size_t>(min(t0 + row, T - 1)) * D + col;
+  }
+  const bf16_t* b_src[PS::kBInst];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-          const float z = (nb == 0 ? acc0[i] : acc1[i]) + b;
-          zs[r][col] = z;
-          if (t0 + r < T) logits[static_cast<size_t>(t0 + r) * E + col] = z;
-        }
+  for (int q = 0; q < PS::kBInst; ++q) {
+    int row, col;
+    dma_chunk<PS::kBInst>(q, row, col);
+    b_src[q] = wr + static_cast<size_t>(min(row, E - 1)) * D + col;
+  }
+  const int brow[2] = {e_base, e_base + 32};
+  f32x16 acc[1][2];
+  mma_pipeline<kRouteTokens, NS>(a_src, b_src, D / kPipeBK, 1, brow, lds, acc);
+
+  float (*zs)[kMaxE + 1] = reinterpret_cast<float (*)[kMaxE + 1]>(lds);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = e_base + 32 * j + (lane & 31);
+    if (col < E) {
+      const float b = bias ? bias[col] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = mfma32_row(r, lane);
+        const float z = acc[0][j][r] + b;
+        zs[row][col] = z;
+        if (t0 + row < T) logits[static_cast<size_t>(t0 + row) * E + col] = z;
       }
     }
   }
@@ -156,7 +173,7 @@ hipError_t launch_route_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* 
                              const float* bias, float* logits, int32_t* idx, float* w,
                              hipStream_t st) {
   const int blocks = (s.T + kRouteTokens - 1) / kRouteTokens;
-  route_bf16_kernel<<<blocks, 256, 0, st>>>(x, wr, bias, logits, idx, w, s.T, s.D, s.E, s.k);
+  route_bf16_kernel<4><<<blocks, 256, 0, st>>>(x, wr, bias, logits, idx, w, s.T, s.D, s.E, s.k);
   return hipGetLastError();
 }
 
