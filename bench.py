@@ -123,14 +123,9 @@ def main():
     wgu, wd = inp.all_experts()
     host = {"x": inp.x, "w_router": inp.w_router, "bias": inp.bias, "wgu": wgu, "wd": wd,
             "shared": inp.shared()}
-    td = lambda a: binding.to_device(a, s, dev)
-    w = binding.LayerWeights(
-        w_router=td(inp.w_router),
-        bias=None if inp.bias is None else torch.from_numpy(inp.bias).to(dev),
-        w_gate_up=td(wgu), w_down=td(wd),
-        ws_gate_up=None if host["shared"] is None else td(host["shared"][0]),
-        ws_down=None if host["shared"] is None else td(host["shared"][1]))
-    x = td(inp.x)
+    # expert weights are packed once into MFMA fragment order (moe_pack_weights)
+    w = binding.upload_weights(s, inp.w_router, inp.bias, wgu, wd, host["shared"], dev)
+    x = binding.to_device(inp.x, s, dev)
     b = binding.alloc_buffers(s, dev, with_x_perm=args.x_perm)
     c = binding.make_shape(s)
     stream = torch.cuda.current_stream(dev)

@@ -37,7 +37,7 @@
  * Shape limits (else MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED):
  *   1 <= E <= 256, 1 <= k <= min(E, 16), T >= 0, T * k < 2^31.
  *   MOE_BF16: D % 256 == 0, F % 128 == 0, Fs % 128 == 0 (Fs == 0 = no shared expert).
- *   MOE_F32:  D % 4 == 0, F % 4 == 0, Fs % 4 == 0.
+ *   MOE_F32:  D % 32 == 0, F % 16 == 0, Fs % 16 == 0, D, F, Fs <= 8192.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -118,6 +118,20 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, 
                 int32_t* offsets, int32_t* sorted_token, int32_t* slot_of, void* x_perm,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Repack weight matrices into MFMA fragment order, the layout every weight
+ * argument of moe_grouped_gate_up / moe_grouped_down / moe_grouped_ffn takes
+ * (a one-time pass when weights are loaded; the pages' experts are the
+ * SwiGLU projections of "Laguna-M.1-base", Feed-forward).
+ *   w         [count, rows, cols] elem, row-major (e.g. w_gate_up as [E, 2F, D])
+ *   w_packed  same number of elements, out; must not overlap w
+ *   rows % 32 == 0, cols % 16 == 0 (else MOE_ERR_INVALID_ARG)
+ * Layout: for each matrix, element (r, c) goes to
+ *   ((r / 32) * (cols / 16) + c / 16) * 512 + ((r % 32) + 32 * ((c % 16) / 8)) * 8 + c % 8,
+ * i.e. 32 x 16 blocks, row-block major, in which 16-byte (bf16) lane chunks
+ * are the operand of one wave for one 32x32x16 MFMA step. */
+int moe_pack_weights(const void* w, void* w_packed, int64_t count, int32_t rows, int32_t cols,
+                     int32_t dtype, void* stream);
+
 /* First grouped GEMM of the experts with the SwiGLU fused in its epilogue
  * ("Laguna-M.1-base", Feed-forward: SwiGLU, no bias; the grouped GEMM over
  * expert-ordered tokens of "Laguna M.1/XS.2 Technical Report", Key claims,
@@ -129,8 +143,9 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, 
  *   sorted_token [k*T] int32 (read only when x_perm is NULL)
  *   x            [T, D] elem
  *   offsets      [E+1] int32 from moe_permute
- *   w_gate_up    [E, 2F, D] elem: rows 0..F-1 = gate projection, F..2F-1 = up
- *   ws_gate_up   [2Fs, D] elem, same split; ignored (may be NULL) when Fs == 0
+ *   w_gate_up    [E, 2F, D] elem, packed per expert (moe_pack_weights): rows
+ *                0..F-1 = gate projection, F..2F-1 = up projection
+ *   ws_gate_up   [2Fs, D] elem, packed, same split; ignored (may be NULL) when Fs == 0
  *   h            [k*T*F + T*Fs] elem out: routed rows [k*T, F], then shared rows [T, Fs]
  * The h values are rounded once to elem (bf16 round-to-nearest-even). */
 int moe_grouped_gate_up(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
@@ -141,8 +156,8 @@ int moe_grouped_gate_up(const moe_shape* shape, const void* x_perm, const int32_
  * y_shared[t] = Wsd hs[t] ("Laguna-M.1-base", Feed-forward: down projection).
  *   h         as written by moe_grouped_gate_up
  *   offsets   [E+1] int32
- *   w_down    [E, D, F] elem
- *   ws_down   [D, Fs] elem (ignored, may be NULL, when Fs == 0)
+ *   w_down    [E, D, F] elem, packed per expert (moe_pack_weights)
+ *   ws_down   [D, Fs] elem, packed (ignored, may be NULL, when Fs == 0)
  *   y_perm    [k*T, D] elem out
  *   y_shared  [T, D] elem out (untouched when Fs == 0; may then be NULL) */
 int moe_grouped_down(const moe_shape* shape, const void* h, const int32_t* offsets,

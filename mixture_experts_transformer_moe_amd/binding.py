@@ -13,6 +13,7 @@ import os
 from dataclasses import dataclass
 from typing import Dict, Optional
 
+import numpy as np
 import torch
 
 from .configs import MoEShape
@@ -24,8 +25,8 @@ MOE_F32, MOE_BF16 = 0, 1
 
 # the entry points include/moe.h declares
 EXPORTS = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
-           "moe_route", "moe_permute", "moe_grouped_gate_up", "moe_grouped_down",
-           "moe_grouped_ffn", "moe_combine")
+           "moe_route", "moe_permute", "moe_pack_weights", "moe_grouped_gate_up",
+           "moe_grouped_down", "moe_grouped_ffn", "moe_combine")
 
 
 class moe_shape(ctypes.Structure):
@@ -65,6 +66,9 @@ def lib() -> ctypes.CDLL:
         L.moe_route.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P]
         L.moe_permute.restype = ctypes.c_int
         L.moe_permute.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_pack_weights.restype = ctypes.c_int
+        L.moe_pack_weights.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, _P]
         L.moe_grouped_gate_up.restype = ctypes.c_int
         L.moe_grouped_gate_up.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_grouped_down.restype = ctypes.c_int
@@ -121,6 +125,23 @@ def moe_permute(shape, topk_idx, x, counts, offsets, sorted_token, slot_of, x_pe
                              _ptr(workspace), nbytes, _stream(stream)), "moe_permute")
 
 
+def moe_pack_weights(w, w_packed, count, rows, cols, dtype, stream=None):
+    _check(lib().moe_pack_weights(_ptr(w), _ptr(w_packed), int(count), int(rows), int(cols), int(dtype),
+                                  _stream(stream)), "moe_pack_weights")
+
+
+def pack(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """Packed copy of a [rows, cols] or [count, rows, cols] weight tensor."""
+    if w.dim() == 2:
+        count, rows, cols = 1, w.shape[0], w.shape[1]
+    else:
+        count, rows, cols = w.shape
+    out = torch.empty_like(w)
+    dtype = MOE_BF16 if w.dtype == torch.bfloat16 else MOE_F32
+    moe_pack_weights(w, out, count, rows, cols, dtype, stream)
+    return out
+
+
 def moe_grouped_gate_up(shape, x_perm, sorted_token, x, offsets, w_gate_up, ws_gate_up, h,
                         stream=None):
     _check(lib().moe_grouped_gate_up(ctypes.byref(shape), _ptr(x_perm), _ptr(sorted_token), _ptr(x),
@@ -157,7 +178,6 @@ def storage_dtype(s: MoEShape) -> torch.dtype:
 
 def to_device(a, s: MoEShape, device) -> torch.Tensor:
     """Storage-encoded numpy array (fp32, or bf16 bits as uint16) -> device tensor."""
-    import numpy as np
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
@@ -206,27 +226,33 @@ def alloc_buffers(s: MoEShape, device="cuda", with_x_perm: bool = True) -> Layer
 
 @dataclass
 class LayerWeights:
+    """Layer weights on the device; expert weights in the packed layout."""
     w_router: torch.Tensor
     bias: Optional[torch.Tensor]
-    w_gate_up: torch.Tensor       # [E, 2F, D]
-    w_down: torch.Tensor          # [E, D, F]
+    w_gate_up: torch.Tensor       # [E, 2F, D], packed per expert
+    w_down: torch.Tensor          # [E, D, F], packed per expert
     ws_gate_up: Optional[torch.Tensor]
     ws_down: Optional[torch.Tensor]
+
+
+def upload_weights(s: MoEShape, w_router, bias, wgu, wd, shared, device="cuda") -> LayerWeights:
+    """Host arrays in storage encoding -> LayerWeights (expert weights packed on the device)."""
+    td = lambda a: to_device(a, s, device)
+    return LayerWeights(
+        w_router=td(w_router),
+        bias=None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).to(device),
+        w_gate_up=pack(td(wgu)),
+        w_down=pack(td(wd)),
+        ws_gate_up=None if shared is None else pack(td(shared[0])),
+        ws_down=None if shared is None else pack(td(shared[1])),
+    )
 
 
 def upload(inputs, device="cuda"):
     """Seeded inputs (``inputs.LayerInputs``) -> (x, LayerWeights) on the device."""
     s = inputs.shape
     wgu, wd = inputs.all_experts()
-    sh = inputs.shared()
-    w = LayerWeights(
-        w_router=to_device(inputs.w_router, s, device),
-        bias=None if inputs.bias is None else torch.from_numpy(inputs.bias).to(device),
-        w_gate_up=to_device(wgu, s, device),
-        w_down=to_device(wd, s, device),
-        ws_gate_up=None if sh is None else to_device(sh[0], s, device),
-        ws_down=None if sh is None else to_device(sh[1], s, device),
-    )
+    w = upload_weights(s, inputs.w_router, inputs.bias, wgu, wd, inputs.shared(), device)
     return to_device(inputs.x, s, device), w
 
 

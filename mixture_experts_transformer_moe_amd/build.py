@@ -20,7 +20,8 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_gemm.hip", "ffn_f32.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_gemm.hip", "ffn_f32.hip", "combine.hip",
+           "pack.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -58,8 +58,8 @@ int check_shape(const moe_shape* s) {
     if (s->F % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: F = %d is not a multiple of 128", s->F);
     if (s->Fs % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: Fs = %d is not a multiple of 128", s->Fs);
   } else {
-    if (s->D % 4 != 0 || s->F % 4 != 0 || s->Fs % 4 != 0)
-      return fail(MOE_ERR_UNSUPPORTED, "fp32: D, F and Fs must be multiples of 4");
+    if (s->D % 32 != 0 || s->F % 16 != 0 || s->Fs % 16 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "fp32: D must be a multiple of 32, F and Fs of 16");
     if (s->D > 8192 || s->F > 8192 || s->Fs > 8192)
       return fail(MOE_ERR_UNSUPPORTED, "fp32: D, F and Fs are limited to 8192");
   }
@@ -213,6 +213,24 @@ int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* s
                                   h, stream))
     return r;
   return moe_grouped_down(shape, h, offsets, w_down, ws_down, y_perm, y_shared, stream);
+}
+
+int moe_pack_weights(const void* w, void* w_packed, int64_t count, int32_t rows, int32_t cols,
+                     int32_t dtype, void* stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "dtype %d is neither MOE_F32 nor MOE_BF16", dtype);
+  if (count < 0 || rows < 0 || cols < 0)
+    return fail(MOE_ERR_INVALID_ARG, "negative count or size");
+  if (rows % 32 != 0 || cols % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "rows = %d must be a multiple of 32 and cols = %d of 16", rows, cols);
+  if (count == 0 || rows == 0 || cols == 0) return ok();
+  NEED_PTR(w);
+  NEED_PTR(w_packed);
+  const int elem = dtype == MOE_BF16 ? 2 : 4;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(w_packed);
+  const uintptr_t bytes = static_cast<uintptr_t>(count) * rows * cols * elem;
+  if (a < b + bytes && b < a + bytes) return fail(MOE_ERR_INVALID_ARG, "w and w_packed overlap");
+  return launched(moe::launch_pack(w, w_packed, count, rows, cols, elem, as_stream(stream)));
 }
 
 int moe_combine(const moe_shape* shape, const void* y_perm, const void* y_shared,

@@ -1,8 +1,8 @@
 // fp32 expert FFN (small fp32 layers, held to 1e-5 relative): one workgroup per
 // expert-ordered row, the row staged in LDS, each thread one output column with
-// fp32 FMA in index order.  Same contract as the bf16 grouped GEMMs
-// ("Laguna-M.1-base", Feed-forward: SwiGLU, no biases).
-#include "moe_internal.h"
+// fp32 FMA in index order.  Same contract as the bf16 grouped GEMMs, weights in
+// the same packed layout ("Laguna-M.1-base", Feed-forward: SwiGLU, no biases).
+#include "mma_stream.h"   // packed_offset
 
 namespace moe {
 namespace {
@@ -50,12 +50,10 @@ __global__ __launch_bounds__(256) void gate_up_f32_kernel(const float* __restric
   for (int d = threadIdx.x; d < D; d += blockDim.x) arow[d] = src[d];
   __syncthreads();
   for (int f = threadIdx.x; f < n; f += blockDim.x) {
-    const float* wg = w + static_cast<size_t>(f) * D;
-    const float* wu = w + static_cast<size_t>(n + f) * D;
     float gv = 0.f, uv = 0.f;
     for (int d = 0; d < D; ++d) {
-      gv = fmaf(wg[d], arow[d], gv);
-      uv = fmaf(wu[d], arow[d], uv);
+      gv = fmaf(w[packed_offset(f, d, D)], arow[d], gv);
+      uv = fmaf(w[packed_offset(n + f, d, D)], arow[d], uv);
     }
     out[f] = gv / (1.0f + expf(-gv)) * uv;
   }
@@ -91,9 +89,8 @@ __global__ __launch_bounds__(256) void down_f32_kernel(const float* __restrict__
   for (int f = threadIdx.x; f < kdim; f += blockDim.x) hrow[f] = src[f];
   __syncthreads();
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    const float* wr = w + static_cast<size_t>(d) * kdim;
     float acc = 0.f;
-    for (int f = 0; f < kdim; ++f) acc = fmaf(wr[f], hrow[f], acc);
+    for (int f = 0; f < kdim; ++f) acc = fmaf(w[packed_offset(d, f, kdim)], hrow[f], acc);
     out[d] = acc;
   }
 }

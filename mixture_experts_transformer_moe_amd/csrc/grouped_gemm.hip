@@ -16,18 +16,18 @@
 //     tile range is cut into 8 contiguous chunks, one per XCD (workgroup b runs
 //     on XCD b % 8), so the workgroups that share a weight tile run at the
 //     same time behind the same L2;
-//   * BM x 256 tiles (BM by the mean rows per expert), one workgroup per CU,
-//     both operands streamed by direct global->LDS loads through a ring of
-//     stages (mma_pipeline.h); gate_up tiles pair each gate block with the up
-//     block of the same columns, so SwiGLU is applied in registers before one
-//     rounding to bf16;
-//   * epilogue staged through LDS for 16-byte coalesced row stores.
-#include "mma_pipeline.h"
+//   * BM x 256 tiles (BM by the mean rows per expert, so an expert's rows
+//     mostly fit one tile and its weights stream once), one workgroup per CU;
+//     weights, packed in MFMA fragment order, stream from HBM straight into
+//     registers through a deep prefetch ring, token rows go through an LDS ring
+//     (mma_stream.h); gate_up tiles pair each gate block with the up block of
+//     the same columns, so SwiGLU is applied in registers before one rounding
+//     to bf16, and results are stored straight from registers.
+#include "mma_stream.h"
 
 namespace moe {
 namespace {
 
-constexpr int BK = kPipeBK;
 constexpr int kThreads = kPipeThreads;
 constexpr int kMaxE = 256;
 constexpr int kXcds = 8;
@@ -49,19 +49,18 @@ struct GemmArgs {
   int has_shared;
 };
 
-// One kernel for both GEMMs: a tile is BM rows of one group x 256 weight rows
-// (gate_up: 128 gate rows and the 128 up rows of the same columns; down: 256
-// output columns); the four waves split the weight rows, 64 each, and run the
-// shared pipeline (mma_pipeline.h).
+// One kernel for both GEMMs: a tile is BM token rows of one group x 256 weight
+// rows (gate_up: 128 gate rows and the 128 up rows of the same columns; down:
+// 256 output columns), computed by the weight-streaming pipeline
+// (mma_stream.h).  Wave w holds the gate block and the up block of the same 32
+// columns, so SwiGLU is applied in registers; outputs go straight from
+// registers to memory, four adjacent bf16 values (8 bytes) per lane and store.
 template <int MODE, int BM, int NS>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
-  using PS = PipeShape<BM, NS>;
-  constexpr int MB = BM / 32;                                   // 32-row MFMA blocks per wave
+  using ST = StreamTile<BM>;
+  constexpr int MBW = ST::MBW;
   constexpr int kOutCols = (MODE == kGateUp) ? 128 : 256;       // output columns per tile
-  constexpr int kStageLd = kOutCols + 8;                        // padded epilogue row
-  constexpr int kHalfRows = BM * kStageLd > PS::kStageElems ? BM / 2 : BM;   // epilogue pass height
-  static_assert(kHalfRows * kStageLd <= PS::kStageElems, "epilogue staging");
-  __shared__ __attribute__((aligned(16))) bf16_t lds[PS::kLdsElems];
+  __shared__ __attribute__((aligned(16))) bf16_t lds[NS * ST::kAElems];
   __shared__ int tile_end[kMaxE + 1];
   __shared__ int row_base[kMaxE + 1];
 
@@ -126,89 +125,77 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     const int n_tile = local / mt;
     const int K = shared ? g.Ks : g.K;
     const int Nout = shared ? g.Ns : g.N;
-    const int NKB = K / BK;
-    const int mb_valid = min(MB, (M - m0 + 31) >> 5);
+    const int n0 = n_tile * kOutCols;
+    const int valid = min(BM, M - m0);
 
-    // ---- DMA sources of this lane (see dma_chunk): A rows, then B rows
-    const bf16_t* a_src[PS::kAInst];
+    // ---- token-row DMA sources of this lane (rows past M clamp; whole 32-row
+    // groups past M are not loaded)
+    const int rb = shared ? 0 : row_base[grp];
+    const bf16_t* a_src[ST::kAGroups];
 #pragma unroll
-    for (int q = 0; q < PS::kAInst; ++q) {
+    for (int gq = 0; gq < ST::kAGroups; ++gq) {
       int row, col;
-      dma_chunk<PS::kAInst>(q, row, col);
-      const int r = min(m0 + row, M - 1);                // rows past M are computed and dropped
+      chunk_source(stream_a_slot(gq, wave, lane), row, col);
+      const int rr = min(m0 + row, M - 1);
       const bf16_t* arow;
       if (shared) {
-        arow = g.a_shared + static_cast<size_t>(r) * K;
+        arow = g.a_shared + static_cast<size_t>(rr) * K;
       } else if (g.gather) {
-        const int t = min(max(g.gather[row_base[grp] + r], 0), g.T - 1);
+        const int t = min(max(g.gather[rb + rr], 0), g.T - 1);
         arow = g.a_routed + static_cast<size_t>(t) * K;
       } else {
-        arow = g.a_routed + static_cast<size_t>(row_base[grp] + r) * K;
+        arow = g.a_routed + static_cast<size_t>(rb + rr) * K;
       }
-      a_src[q] = arow + col;
+      a_src[gq] = arow + col;
     }
+    // ---- packed-weight sources of this lane: the wave's two 32-row blocks
     const bf16_t* wbase = shared ? g.w_shared
                                  : g.w_routed + static_cast<size_t>(grp) * (MODE == kGateUp ? 2 * Nout : Nout) * K;
-    const bf16_t* b_src[PS::kBInst];
-#pragma unroll
-    for (int q = 0; q < PS::kBInst; ++q) {
-      int row, col;
-      dma_chunk<PS::kBInst>(q, row, col);
-      int wrow;
-      if (MODE == kGateUp)   // B rows 0..127: gate rows; 128..255: the up rows of the same columns
-        wrow = (row < 128 ? 0 : Nout - 128) + n_tile * kOutCols + row;
-      else
-        wrow = n_tile * kOutCols + row;
-      b_src[q] = wbase + static_cast<size_t>(wrow) * K + col;
-    }
-    // this wave's two 32-row B blocks inside the tile
-    int brow[2];
-    if (MODE == kGateUp) {
-      brow[0] = 32 * wave;
-      brow[1] = 128 + 32 * wave;
+    int wrow[2];
+    int col0;
+    if (MODE == kGateUp) {           // gate block and the up block of the same 32 columns
+      wrow[0] = n0 + 32 * wave;
+      wrow[1] = Nout + n0 + 32 * wave;
+      col0 = n0 + 32 * wave;
     } else {
-      brow[0] = 64 * wave;
-      brow[1] = 64 * wave + 32;
+      wrow[0] = n0 + 64 * wave;
+      wrow[1] = n0 + 64 * wave + 32;
+      col0 = n0 + 64 * wave;
     }
+    const bf16_t* wsrc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      wsrc[j] = wbase + static_cast<size_t>(wrow[j] >> 5) * (K >> 4) * 512 + lane * 8;
+    bf16_t* out = shared ? g.out_shared : g.out_routed + static_cast<size_t>(rb) * Nout;
 
-    f32x16 acc[MB][2];
-    mma_pipeline<BM, NS>(a_src, b_src, NKB, mb_valid, brow, lds, acc);
-
-    // ---- epilogue: registers -> LDS tile (bf16) -> 16-byte row stores, in
-    // passes of kHalfRows rows through the start of the LDS ring
-    constexpr int kChunksPerRow = kOutCols / 8;
-    bf16_t* out = shared ? g.out_shared : g.out_routed + static_cast<size_t>(row_base[grp]) * Nout;
-    const int n0 = n_tile * kOutCols;
+    stream_pipeline<BM, NS>(a_src, wsrc, K / kStreamBK, valid, lds, [&](auto& acc) {
 #pragma unroll
-    for (int pass = 0; pass < BM / kHalfRows; ++pass) {
+      for (int m = 0; m < MBW; ++m) {
+        const int row = 32 * m + (lane & 31);                   // token row inside the tile
+        if (row < valid) {
+          bf16_t* orow = out + static_cast<size_t>(m0 + row) * Nout + col0 + 4 * (lane >> 5);
 #pragma unroll
-      for (int m = pass * (kHalfRows / 32); m < (pass + 1) * (kHalfRows / 32); ++m) {
+          for (int q = 0; q < 4; ++q) {          // registers 4q..4q+3: 4 adjacent columns
+            if (MODE == kGateUp) {
+              float h[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 32 * m + mfma32_row(r, lane) - pass * kHalfRows;
-          if (MODE == kGateUp) {
-            const int col = 32 * wave + (lane & 31);
-            const float gv = acc[m][0][r], uv = acc[m][1][r];
-            lds[row * kStageLd + col] = f32_to_bf16(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
-          } else {
+              for (int e = 0; e < 4; ++e) {
+                const float gv = acc[m][0][4 * q + e], uv = acc[m][1][4 * q + e];
+                h[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+              }
+              *reinterpret_cast<uint2*>(orow + 8 * q) =
+                  make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+            } else {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const int col = 64 * wave + 32 * j + (lane & 31);
-              lds[row * kStageLd + col] = f32_to_bf16(acc[m][j][r]);
+              for (int j = 0; j < 2; ++j)
+                *reinterpret_cast<uint2*>(orow + 32 * j + 8 * q) =
+                    make_uint2(pack_bf16x2(acc[m][j][4 * q], acc[m][j][4 * q + 1]),
+                               pack_bf16x2(acc[m][j][4 * q + 2], acc[m][j][4 * q + 3]));
             }
           }
         }
       }
-      __syncthreads();
-      const int rows = min(kHalfRows, M - m0 - pass * kHalfRows);
-      for (int c = tid; c < rows * kChunksPerRow; c += kThreads) {
-        const int row = c / kChunksPerRow, ch = c % kChunksPerRow;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&lds[row * kStageLd + ch * 8]);
-        *reinterpret_cast<u32x4*>(out + static_cast<size_t>(m0 + pass * kHalfRows + row) * Nout + n0 +
-                                  ch * 8) = v;
-      }
-      __syncthreads();
-    }
+    });
   }
 }
 
@@ -232,9 +219,11 @@ template <int MODE>
 hipError_t launch_tiles(const GemmArgs& a, const moe_shape& s, hipStream_t st) {
   const int mean_rows = (s.T * s.k) / s.E;
   if (mean_rows >= 96)
-    grouped_gemm_kernel<MODE, 128, 3><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 192, 4><<<persistent_grid(), kThreads, 0, st>>>(a);
   else if (mean_rows >= 48)
-    grouped_gemm_kernel<MODE, 64, 3><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 128, 4><<<persistent_grid(), kThreads, 0, st>>>(a);
+  else if (mean_rows >= 24)
+    grouped_gemm_kernel<MODE, 64, 4><<<persistent_grid(), kThreads, 0, st>>>(a);
   else
     grouped_gemm_kernel<MODE, 32, 4><<<persistent_grid(), kThreads, 0, st>>>(a);
   return hipGetLastError();

@@ -62,6 +62,9 @@ hipError_t launch_down_f32(const moe_shape& s, const float* h, const int32_t* of
                            const float* wd, const float* wsd, float* y_perm, float* y_shared,
                            hipStream_t st);
 
+hipError_t launch_pack(const void* src, void* dst, int64_t count, int rows, int cols, int elem,
+                       hipStream_t st);
+
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_shared,
                           const int32_t* slot_of, const float* topk_w, void* out,
                           hipStream_t st);

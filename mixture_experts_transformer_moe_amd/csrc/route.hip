@@ -94,48 +94,49 @@ __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __rest
                                                             int32_t* __restrict__ idx,
                                                             float* __restrict__ wout, int T, int D,
                                                             int E, int k) {
-  using PS = PipeShape<kRouteTokens, NS>;
-  static_assert(kRouteTokens * (kMaxE + 1) * 2 <= PS::kLdsElems, "logit tile fits the ring");
-  __shared__ __attribute__((aligned(16))) bf16_t lds[PS::kLdsElems];
+  using PT = PipeTile<kRouteTokens, kMaxE>;
+  constexpr int kLdsElems = NS * PT::kStageElems;
+  static_assert(kRouteTokens * (kMaxE + 1) * 2 <= kLdsElems, "logit tile fits the ring");
+  __shared__ __attribute__((aligned(16))) bf16_t lds[kLdsElems];
   const int t0 = blockIdx.x * kRouteTokens;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int e_base = 64 * wave;
+  const int valid = min(kRouteTokens, T - t0);
 
-  const bf16_t* a_src[PS::kAInst];
-#pragma unroll
-  for (int q = 0; q < PS::kAInst; ++q) {
-    int row, col;
-    dma_chunk<PS::kAInst>(q, row, col);
-    a_src[q] = x + static_cast<size_t>(min(t0 + row, T - 1)) * D + col;
-  }
-  const bf16_t* b_src[PS::kBInst];
-#pragma unroll
-  for (int q = 0; q < PS::kBInst; ++q) {
-    int row, col;
-    dma_chunk<PS::kBInst>(q, row, col);
-    b_src[q] = wr + static_cast<size_t>(min(row, E - 1)) * D + col;
-  }
+  const bf16_t* a_src[PT::kAGroups];
+  const bf16_t* b_src[PT::kBInst];
+  pipe_sources<kRouteTokens, kMaxE>(
+      a_src, b_src, [&](int r) { return x + static_cast<size_t>(min(t0 + r, T - 1)) * D; },
+      [&](int r) { return wr + static_cast<size_t>(min(r, E - 1)) * D; });
   const int brow[2] = {e_base, e_base + 32};
-  f32x16 acc[1][2];
-  mma_pipeline<kRouteTokens, NS>(a_src, b_src, D / kPipeBK, 1, brow, lds, acc);
-
   float (*zs)[kMaxE + 1] = reinterpret_cast<float (*)[kMaxE + 1]>(lds);
+  mma_pipeline<kRouteTokens, kMaxE, NS>(a_src, b_src, D / kPipeBK, valid, brow, lds, [&](auto& acc) {
+    // lane: token (lane & 31); register quad q: experts e0 + 8 q + 4 (lane / 32) + 0..3
+    const int row = lane & 31;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = e_base + 32 * j + (lane & 31);
-    if (col < E) {
-      const float b = bias ? bias[col] : 0.f;
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = mfma32_row(r, lane);
-        const float z = acc[0][j][r] + b;
-        zs[row][col] = z;
-        if (t0 + row < T) logits[static_cast<size_t>(t0 + row) * E + col] = z;
+      for (int q = 0; q < 4; ++q) {
+        const int e0 = e_base + 32 * j + 8 * q + 4 * (lane >> 5);
+        float z[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          z[c] = acc[0][j][4 * q + c] + ((bias && e0 + c < E) ? bias[e0 + c] : 0.f);
+          zs[row][e0 + c] = z[c];
+        }
+        if (row < valid && e0 < E) {
+          float* dst = logits + static_cast<size_t>(t0 + row) * E + e0;
+          if (e0 + 4 <= E && (E & 3) == 0) {
+            *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
+          } else {
+            for (int c = 0; c < 4 && e0 + c < E; ++c) dst[c] = z[c];
+          }
+        }
       }
     }
-  }
+  });
   __syncthreads();
   for (int r = wave; r < kRouteTokens; r += 4) {
     const int t = t0 + r;

@@ -38,14 +38,8 @@ class StackedInputs:
 
 def upload_stacked(inp: StackedInputs, device="cuda"):
     s = inp.shape
-    td = lambda a: binding.to_device(a, s, device)
-    w = binding.LayerWeights(
-        w_router=td(inp.w_router),
-        bias=None if inp.bias is None else torch.from_numpy(np.asarray(inp.bias, np.float32)).to(device),
-        w_gate_up=td(inp.wgu), w_down=td(inp.wd),
-        ws_gate_up=None if inp.shared() is None else td(inp.shared()[0]),
-        ws_down=None if inp.shared() is None else td(inp.shared()[1]))
-    return td(inp.x), w
+    w = binding.upload_weights(s, inp.w_router, inp.bias, inp.wgu, inp.wd, inp.shared(), device)
+    return binding.to_device(inp.x, s, device), w
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
