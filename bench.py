@@ -38,6 +38,37 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 
+# HBM bytes of one gate/up launch as read by rocprofv3 (FETCH_SIZE and WRITE_SIZE,
+# KiB per dispatch, one counter per run of this script with --copy-mib 1024),
+# each scaled by what the same counter reads for a plain 1 GiB device copy
+# (FETCH_SIZE reads half of the copy's bytes, WRITE_SIZE all of them).  A record
+# holds only for the kernel sources it was taken on: after any change to them
+# the traffic is reported as null until the counters are taken again.
+FETCH_FACTOR = 2.0
+WRITE_FACTOR = 1.0
+GEMM_SOURCES = ("grouped_gemm.hip", "mma_stream.h", "mma_pipeline.h", "moe_internal.h")
+TRAFFIC = {
+    # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
+    "xs2_bf16_t4096_d2048": (628393.3, 36864.5,
+                             "efbb935ffc682c843b7eb0ef9e0cf6f2cb5a9a8a25da0e1cc67fa7fcfc75cc8d"),
+}
+
+
+def gemm_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_transformer_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    rec = TRAFFIC.get(workload)
+    if rec is None or rec[2] != gemm_sources_sha256():
+        return None
+    return (rec[0] * FETCH_FACTOR + rec[1] * WRITE_FACTOR) * 1024.0
+
 
 def gate_up_work(s: configs.MoEShape, n_touched: int):
     """Algorithmic FLOPs and HBM bytes of one gate/up grouped-GEMM launch.
@@ -106,6 +137,9 @@ def main():
                     help="materialise x_perm in moe_permute and read it in the first GEMM "
                          "(default: the first GEMM gathers token rows through sorted_token)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, copy a buffer of this many MiB device to device "
+                         "three times (a plain copy of known size, to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's "
@@ -158,6 +192,15 @@ def main():
     elapsed = time.perf_counter() - t0
     gate_up_ms = float(np.mean([a.elapsed_time(z) for a, z in evs]))
 
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     counts = b.counts.cpu().numpy()
     n_touched = int(np.count_nonzero(counts))
     flops, nbytes = gate_up_work(s, n_touched)
@@ -172,7 +215,7 @@ def main():
         achieved = flops / (gate_up_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_flops,
                 "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4)}
-    roof.update({"traffic": None, "kernel": "grouped_gemm_kernel<gate_up> (moe_grouped_gate_up)",
+    roof.update({"traffic": measured_traffic(s.name), "kernel": "grouped_gemm_kernel<gate_up> (moe_grouped_gate_up)",
                  "kernel_ms": round(gate_up_ms, 4), "algorithmic_bytes": nbytes,
                  "algorithmic_flops": flops,
                  "mfma_tflops": round(flops / (gate_up_ms * 1e-3) / 1e12, 1)})
