@@ -123,14 +123,21 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, 
  * (a one-time pass when weights are loaded; the pages' experts are the
  * SwiGLU projections of "Laguna-M.1-base", Feed-forward).
  *   w         [count, rows, cols] elem, row-major (e.g. w_gate_up as [E, 2F, D])
- *   w_packed  same number of elements, out; must not overlap w
+ *   w_packed  moe_packed_bytes(count, rows, cols, dtype) bytes, out; must not
+ *             overlap w
  *   rows % 32 == 0, cols % 16 == 0 (else MOE_ERR_INVALID_ARG)
- * Layout: for each matrix, element (r, c) goes to
+ * Layout: matrix i starts at element i * rows * cols; in it, element (r, c)
+ * goes to
  *   ((r / 32) * (cols / 16) + c / 16) * 512 + ((r % 32) + 32 * ((c % 16) / 8)) * 8 + c % 8,
  * i.e. 32 x 16 blocks, row-block major, in which 16-byte (bf16) lane chunks
  * are the operand of one wave for one 32x32x16 MFMA step. */
 int moe_pack_weights(const void* w, void* w_packed, int64_t count, int32_t rows, int32_t cols,
                      int32_t dtype, void* stream);
+
+/* Size in bytes of `count` packed [rows, cols] matrices of type dtype (the
+ * same as unpacked: count * rows * cols * element size); 0 for sizes
+ * moe_pack_weights rejects. */
+size_t moe_packed_bytes(int64_t count, int32_t rows, int32_t cols, int32_t dtype);
 
 /* First grouped GEMM of the experts with the SwiGLU fused in its epilogue
  * ("Laguna-M.1-base", Feed-forward: SwiGLU, no bias; the grouped GEMM over
@@ -143,9 +150,10 @@ int moe_pack_weights(const void* w, void* w_packed, int64_t count, int32_t rows,
  *   sorted_token [k*T] int32 (read only when x_perm is NULL)
  *   x            [T, D] elem
  *   offsets      [E+1] int32 from moe_permute
- *   w_gate_up    [E, 2F, D] elem, packed per expert (moe_pack_weights): rows
- *                0..F-1 = gate projection, F..2F-1 = up projection
- *   ws_gate_up   [2Fs, D] elem, packed, same split; ignored (may be NULL) when Fs == 0
+ *   w_gate_up    E matrices [2F, D] elem, packed (moe_pack_weights, count E):
+ *                rows 0..F-1 = gate projection, F..2F-1 = up projection
+ *   ws_gate_up   one matrix [2Fs, D] elem, packed, same split; ignored (may be
+ *                NULL) when Fs == 0
  *   h            [k*T*F + T*Fs] elem out: routed rows [k*T, F], then shared rows [T, Fs]
  * The h values are rounded once to elem (bf16 round-to-nearest-even). */
 int moe_grouped_gate_up(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
@@ -156,8 +164,8 @@ int moe_grouped_gate_up(const moe_shape* shape, const void* x_perm, const int32_
  * y_shared[t] = Wsd hs[t] ("Laguna-M.1-base", Feed-forward: down projection).
  *   h         as written by moe_grouped_gate_up
  *   offsets   [E+1] int32
- *   w_down    [E, D, F] elem, packed per expert (moe_pack_weights)
- *   ws_down   [D, Fs] elem, packed (ignored, may be NULL, when Fs == 0)
+ *   w_down    E matrices [D, F] elem, packed (moe_pack_weights, count E)
+ *   ws_down   one matrix [D, Fs] elem, packed (ignored, may be NULL, when Fs == 0)
  *   y_perm    [k*T, D] elem out
  *   y_shared  [T, D] elem out (untouched when Fs == 0; may then be NULL) */
 int moe_grouped_down(const moe_shape* shape, const void* h, const int32_t* offsets,

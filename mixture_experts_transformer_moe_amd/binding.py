@@ -25,7 +25,7 @@ MOE_F32, MOE_BF16 = 0, 1
 
 # the entry points include/moe.h declares
 EXPORTS = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
-           "moe_route", "moe_permute", "moe_pack_weights", "moe_grouped_gate_up",
+           "moe_route", "moe_permute", "moe_pack_weights", "moe_packed_bytes", "moe_grouped_gate_up",
            "moe_grouped_down", "moe_grouped_ffn", "moe_combine")
 
 
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.moe_pack_weights.restype = ctypes.c_int
         L.moe_pack_weights.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, _P]
+        L.moe_packed_bytes.restype = ctypes.c_size_t
+        L.moe_packed_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         L.moe_grouped_gate_up.restype = ctypes.c_int
         L.moe_grouped_gate_up.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_grouped_down.restype = ctypes.c_int
@@ -130,15 +132,23 @@ def moe_pack_weights(w, w_packed, count, rows, cols, dtype, stream=None):
                                   _stream(stream)), "moe_pack_weights")
 
 
+def moe_packed_bytes(count, rows, cols, dtype) -> int:
+    return int(lib().moe_packed_bytes(int(count), int(rows), int(cols), int(dtype)))
+
+
 def pack(w: torch.Tensor, stream=None) -> torch.Tensor:
-    """Packed copy of a [rows, cols] or [count, rows, cols] weight tensor."""
+    """Packed copy of a [rows, cols] or [count, rows, cols] weight tensor (a flat
+    tensor of w's dtype holding moe_packed_bytes bytes)."""
     if w.dim() == 2:
         count, rows, cols = 1, w.shape[0], w.shape[1]
     else:
         count, rows, cols = w.shape
-    out = torch.empty_like(w)
     dtype = MOE_BF16 if w.dtype == torch.bfloat16 else MOE_F32
-    moe_pack_weights(w, out, count, rows, cols, dtype, stream)
+    nbytes = moe_packed_bytes(count, rows, cols, dtype)
+    if nbytes == 0 and count * rows * cols > 0:
+        raise MoEError(MOE_ERR_INVALID_ARG, f"moe_packed_bytes: cannot pack [{count}, {rows}, {cols}]")
+    out = torch.empty(nbytes // w.element_size(), dtype=w.dtype, device=w.device)
+    moe_pack_weights(w.contiguous(), out, count, rows, cols, dtype, stream)
     return out
 
 
@@ -229,8 +239,8 @@ class LayerWeights:
     """Layer weights on the device; expert weights in the packed layout."""
     w_router: torch.Tensor
     bias: Optional[torch.Tensor]
-    w_gate_up: torch.Tensor       # [E, 2F, D], packed per expert
-    w_down: torch.Tensor          # [E, D, F], packed per expert
+    w_gate_up: torch.Tensor       # E packed [2F, D] matrices (flat)
+    w_down: torch.Tensor          # E packed [D, F] matrices (flat)
     ws_gate_up: Optional[torch.Tensor]
     ws_down: Optional[torch.Tensor]
 

@@ -215,6 +215,13 @@ int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* s
   return moe_grouped_down(shape, h, offsets, w_down, ws_down, y_perm, y_shared, stream);
 }
 
+size_t moe_packed_bytes(int64_t count, int32_t rows, int32_t cols, int32_t dtype) {
+  if ((dtype != MOE_F32 && dtype != MOE_BF16) || count < 0 || rows < 0 || cols < 0 || rows % 32 != 0 ||
+      cols % 16 != 0)
+    return 0;
+  return static_cast<size_t>(count) * moe::packed_matrix_elems(rows, cols) * (dtype == MOE_BF16 ? 2 : 4);
+}
+
 int moe_pack_weights(const void* w, void* w_packed, int64_t count, int32_t rows, int32_t cols,
                      int32_t dtype, void* stream) {
   if (dtype != MOE_F32 && dtype != MOE_BF16)
@@ -228,8 +235,9 @@ int moe_pack_weights(const void* w, void* w_packed, int64_t count, int32_t rows,
   NEED_PTR(w_packed);
   const int elem = dtype == MOE_BF16 ? 2 : 4;
   const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(w_packed);
-  const uintptr_t bytes = static_cast<uintptr_t>(count) * rows * cols * elem;
-  if (a < b + bytes && b < a + bytes) return fail(MOE_ERR_INVALID_ARG, "w and w_packed overlap");
+  const uintptr_t in_bytes = static_cast<uintptr_t>(count) * rows * cols * elem;
+  const uintptr_t out_bytes = moe_packed_bytes(count, rows, cols, dtype);
+  if (a < b + out_bytes && b < a + in_bytes) return fail(MOE_ERR_INVALID_ARG, "w and w_packed overlap");
   return launched(moe::launch_pack(w, w_packed, count, rows, cols, elem, as_stream(stream)));
 }
 

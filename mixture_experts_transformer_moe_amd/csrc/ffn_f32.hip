@@ -2,7 +2,7 @@
 // expert-ordered row, the row staged in LDS, each thread one output column with
 // fp32 FMA in index order.  Same contract as the bf16 grouped GEMMs, weights in
 // the same packed layout ("Laguna-M.1-base", Feed-forward: SwiGLU, no biases).
-#include "mma_stream.h"   // packed_offset
+#include "moe_internal.h"   // packed_offset
 
 namespace moe {
 namespace {
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void gate_up_f32_kernel(const float* __restric
     const int e = expert_of(offsets, E, p);
     src = gather ? x + static_cast<size_t>(min(max(gather[p], 0), T - 1)) * D
                  : a_routed + static_cast<size_t>(p) * D;
-    w = wgu + static_cast<size_t>(e) * 2 * F * D;
+    w = wgu + static_cast<size_t>(e) * packed_matrix_elems(2 * F, D);
     n = F;
     out = h + static_cast<size_t>(p) * F;
   } else {
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void down_f32_kernel(const float* __restrict__
   if (!shared) {
     const int e = expert_of(offsets, E, p);
     src = h + static_cast<size_t>(p) * F;
-    w = wd + static_cast<size_t>(e) * D * F;
+    w = wd + static_cast<size_t>(e) * packed_matrix_elems(D, F);
     kdim = F;
     out = y_perm + static_cast<size_t>(p) * D;
   } else {

@@ -12,10 +12,13 @@
 //   * persistent grid: every workgroup derives the tile table from `offsets`
 //     in LDS (tiles per group, inclusive scan), so no host synchronisation and
 //     no extra launch are needed for ragged expert sizes;
-//   * tile order: m-tiles of the same (group, n-tile) are adjacent, and the
-//     tile range is cut into 8 contiguous chunks, one per XCD (workgroup b runs
-//     on XCD b % 8), so the workgroups that share a weight tile run at the
-//     same time behind the same L2;
+//   * tile order: m-tiles of the same (group, n-tile) are adjacent; tiles go
+//     out in rounds of one per workgroup, and each round is cut into 8 runs
+//     of consecutive tiles, one per XCD (workgroup b runs on XCD b % 8), so
+//     the workgroups that share a weight tile run at the same time behind the
+//     same L2, and every workgroup gets the same number of tiles to within
+//     one; the shared expert's row-block height is picked so that its tiles
+//     fill the last round;
 //   * BM x 256 tiles (BM by the mean rows per expert, so an expert's rows
 //     mostly fit one tile and its weights stream once), one workgroup per CU;
 //     weights, packed in MFMA fragment order, stream from HBM straight into
@@ -38,8 +41,8 @@ struct GemmArgs {
   const bf16_t* a_routed;   // [S, K] rows in expert order (x_perm or h), or x when gather != null
   const int32_t* gather;    // sorted_token (A row p = x[gather[p]]) or null
   const bf16_t* a_shared;   // [T, Ks]
-  const bf16_t* w_routed;   // [E, Nw, K]
-  const bf16_t* w_shared;   // [Nws, Ks]
+  const bf16_t* w_routed;   // E packed [Nw, K] matrices
+  const bf16_t* w_shared;   // packed [Nws, Ks]
   bf16_t* out_routed;       // [S, N]
   bf16_t* out_shared;       // [T, Ns]
   const int32_t* offsets;   // [E + 1]
@@ -70,6 +73,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   const int nt_s = g.has_shared ? g.Ns / kOutCols : 0;
 
   // ---- tile table: tiles per routed group, inclusive scan, shared group last
+  __shared__ int shared_bm;
+  const int G = gridDim.x;                 // workgroups, a multiple of kXcds
   {
     int cnt = 0;
     if (tid < E) {
@@ -89,26 +94,41 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     }
     if (tid == 0) {
       const int routed_total = tile_end[E - 1];
-      tile_end[E] = routed_total + (g.has_shared ? (g.T + BM - 1) / BM * nt_s : 0);
+      // Shared-expert row-block height: the tiles run in rounds of G (one per
+      // workgroup), routed tiles first, so the shared tiles fill the last
+      // rounds.  Take the fewest rounds, and for that count the shortest
+      // blocks: the shared weights are read by every block of a round from
+      // L2, and shorter blocks spread them evenly over the workgroups.
+      int best_bm = BM, best_rounds = 0x7fffffff;
+      if (g.has_shared) {
+        for (int bm = 32; bm <= BM; bm += 32) {
+          const int rounds = (routed_total + (g.T + bm - 1) / bm * nt_s + G - 1) / G;
+          if (rounds < best_rounds) {
+            best_rounds = rounds;
+            best_bm = bm;
+          }
+        }
+      }
+      shared_bm = best_bm;
+      tile_end[E] = routed_total + (g.has_shared ? (g.T + best_bm - 1) / best_bm * nt_s : 0);
       row_base[E] = min(max(g.offsets[E], row_base[E - 1]), g.S);
     }
     __syncthreads();
   }
   const int total = tile_end[E];
+  const int sbm = shared_bm;
 
-  // ---- XCD-aware persistent assignment
-  const int P = gridDim.x;                 // multiple of kXcds
-  const int per_xcd = P / kXcds;
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int chunk = (total + kXcds - 1) / kXcds;
-  const int t_lo = xcd * chunk;
-  const int t_hi = min(total, t_lo + chunk);
+  // ---- XCD-aware persistent assignment: tiles go out in rounds of G; inside a
+  // round, workgroup b (on XCD b % 8) takes position (b % 8) * (G / 8) + b / 8,
+  // so each XCD runs a run of G / 8 consecutive tiles -- the row blocks of the
+  // same weights -- at the same time, and no workgroup gets more than one tile
+  // more than another.
+  const int pos = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
 
   const int wave = tid >> 6;
   const int lane = tid & 63;
 
-  for (int ti = t_lo + slot; ti < t_hi; ti += per_xcd) {
+  for (int ti = pos; ti < total; ti += G) {
     // group of this tile: first g with tile_end[g] > ti
     int lo = 0, hi = E;
     while (lo < hi) {
@@ -119,14 +139,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     const bool shared = grp == E;
     const int first = grp == 0 ? 0 : tile_end[grp - 1];
     const int M = shared ? g.T : row_base[grp + 1] - row_base[grp];
-    const int mt = (M + BM - 1) / BM;
+    const int bm = shared ? sbm : BM;      // row-block height of this group
+    const int mt = (M + bm - 1) / bm;
     const int local = ti - first;
-    const int m0 = (local % mt) * BM;
+    const int m0 = (local % mt) * bm;
     const int n_tile = local / mt;
     const int K = shared ? g.Ks : g.K;
     const int Nout = shared ? g.Ns : g.N;
     const int n0 = n_tile * kOutCols;
-    const int valid = min(BM, M - m0);
+    const int valid = min(bm, M - m0);
 
     // ---- token-row DMA sources of this lane (rows past M clamp; whole 32-row
     // groups past M are not loaded)
@@ -149,8 +170,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       a_src[gq] = arow + col;
     }
     // ---- packed-weight sources of this lane: the wave's two 32-row blocks
-    const bf16_t* wbase = shared ? g.w_shared
-                                 : g.w_routed + static_cast<size_t>(grp) * (MODE == kGateUp ? 2 * Nout : Nout) * K;
+    const bf16_t* wbase =
+        shared ? g.w_shared
+               : g.w_routed + static_cast<size_t>(grp) * packed_matrix_elems(MODE == kGateUp ? 2 * Nout : Nout, K);
     int wrow[2];
     int col0;
     if (MODE == kGateUp) {           // gate block and the up block of the same 32 columns

@@ -34,14 +34,6 @@ namespace moe {
 constexpr int kStreamBK = 64;        // K per LDS stage (4 MFMA steps)
 constexpr int kStreamRows = 256;     // weight rows per tile (4 waves x 2 blocks)
 
-// Element offset of weight (row, k) inside a packed [rows x K] matrix:
-// block (row / 32, k / 16) is 512 contiguous elements; in it, lane
-// (row % 32) + 32 ((k % 16) / 8) holds elements k % 8 = 0..7.
-__host__ __device__ __forceinline__ size_t packed_offset(int row, int k, int K) {
-  const size_t blk = static_cast<size_t>(row >> 5) * (K >> 4) + (k >> 4);
-  return blk * 512 + ((row & 31) + 32 * ((k >> 3) & 1)) * 8 + (k & 7);
-}
-
 template <int BM>
 struct StreamTile {
   static constexpr int MBW = BM / 32;             // token blocks (every wave covers all)

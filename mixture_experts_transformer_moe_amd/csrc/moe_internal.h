@@ -62,6 +62,18 @@ hipError_t launch_down_f32(const moe_shape& s, const float* h, const int32_t* of
                            const float* wd, const float* wsd, float* y_perm, float* y_shared,
                            hipStream_t st);
 
+// Packed [rows x K] weight matrix (moe_pack_weights): block (row / 32, k / 16)
+// is 512 contiguous elements, in which lane (row % 32) + 32 ((k % 16) / 8)
+// holds elements k % 8 = 0..7; blocks are row-block major.
+__host__ __device__ __forceinline__ size_t packed_matrix_elems(int rows, int K) {
+  return static_cast<size_t>(rows) * K;
+}
+
+__host__ __device__ __forceinline__ size_t packed_offset(int row, int k, int K) {
+  const size_t blk = static_cast<size_t>(row >> 5) * (K >> 4) + (k >> 4);
+  return blk * 512 + ((row & 31) + 32 * ((k >> 3) & 1)) * 8 + (k & 7);
+}
+
 hipError_t launch_pack(const void* src, void* dst, int64_t count, int rows, int cols, int elem,
                        hipStream_t st);
 

@@ -101,3 +101,23 @@ def test_empty_batch_is_a_no_op(L):
     s = _shape(T=0)
     assert _route(L, s, ptr=0) == binding.MOE_OK
     assert L.moe_combine(ctypes.byref(s), None, None, None, None, None, None) == binding.MOE_OK
+
+
+def test_packed_sizes_and_pack_argument_checks(L):
+    # packing permutes elements inside each matrix: the size is unchanged
+    assert L.moe_packed_bytes(1, 32, 16, binding.MOE_BF16) == 512 * 2
+    assert L.moe_packed_bytes(256, 1024, 2048, binding.MOE_BF16) == 256 * 1024 * 2048 * 2
+    assert L.moe_packed_bytes(3, 64, 48, binding.MOE_F32) == 3 * 64 * 48 * 4
+    assert L.moe_packed_bytes(0, 64, 48, binding.MOE_F32) == 0
+    for bad in ((1, 33, 16, binding.MOE_BF16), (1, 32, 20, binding.MOE_BF16), (1, 32, 16, 7),
+                (-1, 32, 16, binding.MOE_BF16)):
+        assert L.moe_packed_bytes(*bad) == 0
+    p, q = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 30)
+    assert L.moe_pack_weights(p, q, 1, 33, 16, binding.MOE_BF16, None) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(p, q, 1, 32, 16, 5, None) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(None, q, 1, 32, 16, binding.MOE_BF16, None) == binding.MOE_ERR_INVALID_ARG
+    # an output that starts inside the input overlaps it
+    assert L.moe_pack_weights(p, ctypes.c_void_p((1 << 20) + 512), 1, 32, 16, binding.MOE_BF16,
+                              None) == binding.MOE_ERR_INVALID_ARG
+    assert b"overlap" in L.moe_last_error()
+    assert L.moe_pack_weights(p, q, 0, 32, 16, binding.MOE_BF16, None) == binding.MOE_OK

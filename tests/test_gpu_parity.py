@@ -192,3 +192,37 @@ def test_invalid_arguments_raise_without_launch():
     with pytest.raises(binding.MoEError):
         binding.moe_permute(binding.make_shape(s), b.topk_idx, b.out, b.counts, b.offsets,
                             b.sorted_token, b.slot_of, None, small_ws)
+
+
+def _packed_reference(w: np.ndarray) -> np.ndarray:
+    """The layout include/moe.h documents for moe_pack_weights, element by element."""
+    count, rows, cols = w.shape
+    per = rows * cols
+    out = np.zeros(count * per, dtype=w.dtype)
+    for i in range(count):
+        for r in range(rows):
+            for c in range(cols):
+                o = ((r // 32) * (cols // 16) + c // 16) * 512 + ((r % 32) + 32 * ((c % 16) // 8)) * 8 + c % 8
+                out[i * per + o] = w[i, r, c]
+    return out
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_pack_weights_layout_and_padding(dtype):
+    say(f"pack layout {dtype}")
+    rng = np.random.default_rng(7)
+    count, rows, cols = 3, 64, 48
+    if dtype == torch.bfloat16:
+        host = rng.integers(1, 1 << 15, size=(count, rows, cols), dtype=np.int64).astype(np.int16)
+        w = torch.from_numpy(host).view(torch.bfloat16).cuda()
+    else:
+        host = rng.standard_normal((count, rows, cols)).astype(np.float32)
+        w = torch.from_numpy(host).cuda()
+    code = binding.MOE_BF16 if dtype == torch.bfloat16 else binding.MOE_F32
+    n = binding.moe_packed_bytes(count, rows, cols, code) // w.element_size()
+    big, out = _guarded_like(torch.empty(n, dtype=dtype, device="cuda"))
+    binding.moe_pack_weights(w, out, count, rows, cols, code)
+    torch.cuda.synchronize()
+    assert _guard_intact(big, n), "write past the end of the packed buffer"
+    got = out.cpu().view(torch.int16 if dtype == torch.bfloat16 else torch.float32).numpy()
+    assert np.array_equal(got, _packed_reference(host))
