@@ -36,7 +36,8 @@
  *
  * Shape limits (else MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED):
  *   1 <= E <= 256, 1 <= k <= min(E, 16), T >= 0, T * k < 2^31.
- *   MOE_BF16: D % 256 == 0, F % 128 == 0, Fs % 128 == 0 (Fs == 0 = no shared expert).
+ *   MOE_BF16: D % 256 == 0, F % 256 == 0, Fs % 256 == 0 (Fs == 0 = no shared expert),
+ *             T * D < 2^31, T * Fs < 2^31.
  *   MOE_F32:  D % 32 == 0, F % 16 == 0, Fs % 16 == 0, D, F, Fs <= 8192.
  */
 #ifndef MOE_H_

@@ -55,8 +55,14 @@ int check_shape(const moe_shape* s) {
     return fail(MOE_ERR_UNSUPPORTED, "k*T = %lld does not fit int32", static_cast<long long>(s->T) * s->k);
   if (s->dtype == MOE_BF16) {
     if (s->D % 256 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: D = %d is not a multiple of 256", s->D);
-    if (s->F % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: F = %d is not a multiple of 128", s->F);
-    if (s->Fs % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: Fs = %d is not a multiple of 128", s->Fs);
+    // every GEMM reduction (D, F, Fs) is a whole number of 256-wide weight
+    // prefetch rounds; output tiles are 128 (gate/up) and 256 (down) wide
+    if (s->F % 256 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: F = %d is not a multiple of 256", s->F);
+    if (s->Fs % 256 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16: Fs = %d is not a multiple of 256", s->Fs);
+    // token rows are addressed by 32-bit byte offsets
+    if (static_cast<int64_t>(s->T) * s->D * 2 >= (int64_t{1} << 32) ||
+        static_cast<int64_t>(s->T) * s->Fs * 2 >= (int64_t{1} << 32))
+      return fail(MOE_ERR_UNSUPPORTED, "bf16: T * D and T * Fs must stay below 2^31");
   } else {
     if (s->D % 32 != 0 || s->F % 16 != 0 || s->Fs % 16 != 0)
       return fail(MOE_ERR_UNSUPPORTED, "fp32: D must be a multiple of 32, F and Fs of 16");

@@ -52,29 +52,36 @@ struct GemmArgs {
   int has_shared;
 };
 
+// Output side of one tile.
+struct TileOut {
+  bf16_t* out;      // element (row r of the tile, column c of its 256) at out + r * ld + c
+  int ld;
+  int valid;        // rows of the tile that hold tokens
+};
+
 // One kernel for both GEMMs: a tile is BM token rows of one group x 256 weight
 // rows (gate_up: 128 gate rows and the 128 up rows of the same columns; down:
 // 256 output columns), computed by the weight-streaming pipeline
 // (mma_stream.h).  Wave w holds the gate block and the up block of the same 32
 // columns, so SwiGLU is applied in registers; outputs go straight from
 // registers to memory, four adjacent bf16 values (8 bytes) per lane and store.
-template <int MODE, int BM, int NS>
+template <int MODE, int BM>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   using ST = StreamTile<BM>;
   constexpr int MBW = ST::MBW;
   constexpr int kOutCols = (MODE == kGateUp) ? 128 : 256;       // output columns per tile
-  __shared__ __attribute__((aligned(16))) bf16_t lds[NS * ST::kAElems];
+  __shared__ __attribute__((aligned(16))) bf16_t lds[kStreamNS * ST::kAElems];
   __shared__ int tile_end[kMaxE + 1];
   __shared__ int row_base[kMaxE + 1];
+  __shared__ int shared_bm;
 
   const int tid = threadIdx.x;
   const int E = g.E;
   const int nt_r = g.N / kOutCols;
   const int nt_s = g.has_shared ? g.Ns / kOutCols : 0;
+  const int G = gridDim.x;                 // workgroups, a multiple of kXcds
 
   // ---- tile table: tiles per routed group, inclusive scan, shared group last
-  __shared__ int shared_bm;
-  const int G = gridDim.x;                 // workgroups, a multiple of kXcds
   {
     int cnt = 0;
     if (tid < E) {
@@ -115,8 +122,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     }
     __syncthreads();
   }
-  const int total = tile_end[E];
-  const int sbm = shared_bm;
+  const int total = __builtin_amdgcn_readfirstlane(tile_end[E]);
+  const int sbm = __builtin_amdgcn_readfirstlane(shared_bm);
 
   // ---- XCD-aware persistent assignment: tiles go out in rounds of G; inside a
   // round, workgroup b (on XCD b % 8) takes position (b % 8) * (G / 8) + b / 8,
@@ -124,22 +131,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   // same weights -- at the same time, and no workgroup gets more than one tile
   // more than another.
   const int pos = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+  if (pos >= total) return;
 
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
 
-  for (int ti = pos; ti < total; ti += G) {
-    // group of this tile: first g with tile_end[g] > ti
-    int lo = 0, hi = E;
+  // ---- sources and output of tile ti (all but the token-row offsets uniform)
+  auto decode = [&](int ti, StreamSrc<BM>& src, TileOut& o) {
+    int lo = 0, hi = E;                     // group: first with tile_end > ti
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (tile_end[mid] > ti) hi = mid; else lo = mid + 1;
     }
-    const int grp = lo;
+    const int grp = __builtin_amdgcn_readfirstlane(lo);
     const bool shared = grp == E;
-    const int first = grp == 0 ? 0 : tile_end[grp - 1];
-    const int M = shared ? g.T : row_base[grp + 1] - row_base[grp];
-    const int bm = shared ? sbm : BM;      // row-block height of this group
+    const int first = grp == 0 ? 0 : __builtin_amdgcn_readfirstlane(tile_end[grp - 1]);
+    const int rb = shared ? 0 : __builtin_amdgcn_readfirstlane(row_base[grp]);
+    const int M = shared ? g.T : __builtin_amdgcn_readfirstlane(row_base[grp + 1]) - rb;
+    const int bm = shared ? sbm : BM;       // row-block height of this group
     const int mt = (M + bm - 1) / bm;
     const int local = ti - first;
     const int m0 = (local % mt) * bm;
@@ -148,77 +157,120 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     const int Nout = shared ? g.Ns : g.N;
     const int n0 = n_tile * kOutCols;
     const int valid = min(bm, M - m0);
+    src.groups = (valid + 31) >> 5;
+    src.nkb = K / kStreamBK;
 
-    // ---- token-row DMA sources of this lane (rows past M clamp; whole 32-row
-    // groups past M are not loaded)
-    const int rb = shared ? 0 : row_base[grp];
-    const bf16_t* a_src[ST::kAGroups];
-#pragma unroll
-    for (int gq = 0; gq < ST::kAGroups; ++gq) {
-      int row, col;
-      chunk_source(stream_a_slot(gq, wave, lane), row, col);
-      const int rr = min(m0 + row, M - 1);
-      const bf16_t* arow;
-      if (shared) {
-        arow = g.a_shared + static_cast<size_t>(rr) * K;
-      } else if (g.gather) {
-        const int t = min(max(g.gather[rb + rr], 0), g.T - 1);
-        arow = g.a_routed + static_cast<size_t>(t) * K;
-      } else {
-        arow = g.a_routed + static_cast<size_t>(rb + rr) * K;
-      }
-      a_src[gq] = arow + col;
+    // token rows: lane's chunk of LDS load q is row 8 (MBW wave + q) + lane / 8
+    // of the tile (rows past the tile's last one repeat it)
+    const bool gathered = !shared && g.gather != nullptr;
+    if (gathered) {
+      src.a_base = g.a_routed;
+    } else if (shared) {
+      src.a_base = g.a_shared + static_cast<size_t>(m0) * K;
+    } else {
+      src.a_base = g.a_routed + static_cast<size_t>(rb + m0) * K;
     }
-    // ---- packed-weight sources of this lane: the wave's two 32-row blocks
+    // gathered rows: the token ids of the wave's 8 MBW consecutive rows come
+    // in one window of scalar loads (no vector-memory wait, which would also
+    // wait for the weight stream in flight); rows past the expert's last read
+    // other experts' (valid) ids and are dropped.  A window that would run
+    // past the end of the array (only near the last rows) reads per lane.
+    const int wstart = rb + m0 + 8 * MBW * wave;
+    const bool window = gathered && wstart + 8 * MBW <= g.S;
+    int win[8 * MBW];
+    if (window) {
+      const __attribute__((address_space(4))) int32_t* gt =
+          (const __attribute__((address_space(4))) int32_t*)(g.gather) + wstart;
+#pragma unroll
+      for (int i = 0; i < 8 * MBW; ++i) win[i] = gt[i];
+    }
+#pragma unroll
+    for (int q = 0; q < MBW; ++q) {
+      int row, col;
+      chunk_source(stream_a_slot<BM>(q, wave, lane), row, col);
+      uint32_t r;
+      if (gathered) {
+        int tok;
+        if (window) {
+          tok = win[8 * q];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) tok = (lane >> 3) == i ? win[8 * q + i] : tok;
+        } else {
+          tok = g.gather[rb + min(m0 + row, M - 1)];
+        }
+        r = static_cast<uint32_t>(min(max(tok, 0), g.T - 1));
+      } else {
+        r = static_cast<uint32_t>(min(row, valid - 1));
+      }
+      src.a_off[q] = (r * static_cast<uint32_t>(K) + static_cast<uint32_t>(col)) * 2u;
+    }
+    // packed weights: the wave's two 32-row blocks
     const bf16_t* wbase =
         shared ? g.w_shared
                : g.w_routed + static_cast<size_t>(grp) * packed_matrix_elems(MODE == kGateUp ? 2 * Nout : Nout, K);
-    int wrow[2];
-    int col0;
+    int wrow0, wrow1, col0;
     if (MODE == kGateUp) {           // gate block and the up block of the same 32 columns
-      wrow[0] = n0 + 32 * wave;
-      wrow[1] = Nout + n0 + 32 * wave;
+      wrow0 = n0 + 32 * wave;
+      wrow1 = Nout + n0 + 32 * wave;
       col0 = n0 + 32 * wave;
     } else {
-      wrow[0] = n0 + 64 * wave;
-      wrow[1] = n0 + 64 * wave + 32;
+      wrow0 = n0 + 64 * wave;
+      wrow1 = n0 + 64 * wave + 32;
       col0 = n0 + 64 * wave;
     }
-    const bf16_t* wsrc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      wsrc[j] = wbase + static_cast<size_t>(wrow[j] >> 5) * (K >> 4) * 512 + lane * 8;
-    bf16_t* out = shared ? g.out_shared : g.out_routed + static_cast<size_t>(rb) * Nout;
+    src.w[0] = wbase + static_cast<size_t>(wrow0 >> 5) * (K >> 4) * 512;
+    src.w[1] = wbase + static_cast<size_t>(wrow1 >> 5) * (K >> 4) * 512;
+    o.out = (shared ? g.out_shared + static_cast<size_t>(m0) * Nout
+                    : g.out_routed + static_cast<size_t>(rb + m0) * Nout) + col0;
+    o.ld = Nout;
+    o.valid = valid;
+  };
 
-    stream_pipeline<BM, NS>(a_src, wsrc, K / kStreamBK, valid, lds, [&](auto& acc) {
+  StreamSrc<BM> cur, nxt;
+  TileOut ocur, onxt;
+  StreamState ss;
+  decode(pos, cur, ocur);
+  stream_start<BM>(cur, ss, lds);
+  for (int ti = pos; ti < total; ti += G) {
+    const TileOut o = ocur;
+    f32x16 acc[MBW][2];
+    stream_tile<BM>(cur, nxt, [&]() {
+      if (ti + G >= total) return false;
+      decode(ti + G, nxt, onxt);
+      return true;
+    }, ss, lds, acc);
+    // epilogue: registers to memory; no LDS (other waves may still read the
+    // tile's last stage until the next tile's first barrier)
 #pragma unroll
-      for (int m = 0; m < MBW; ++m) {
-        const int row = 32 * m + (lane & 31);                   // token row inside the tile
-        if (row < valid) {
-          bf16_t* orow = out + static_cast<size_t>(m0 + row) * Nout + col0 + 4 * (lane >> 5);
+    for (int m = 0; m < MBW; ++m) {
+      const int row = 32 * m + (lane & 31);                     // token row inside the tile
+      if (row < o.valid) {
+        bf16_t* orow = o.out + static_cast<size_t>(row) * o.ld + 4 * (lane >> 5);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {          // registers 4q..4q+3: 4 adjacent columns
-            if (MODE == kGateUp) {
-              float h[4];
+        for (int q = 0; q < 4; ++q) {            // registers 4q..4q+3: 4 adjacent columns
+          if (MODE == kGateUp) {
+            float h[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float gv = acc[m][0][4 * q + e], uv = acc[m][1][4 * q + e];
-                h[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-              }
-              *reinterpret_cast<uint2*>(orow + 8 * q) =
-                  make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-            } else {
-#pragma unroll
-              for (int j = 0; j < 2; ++j)
-                *reinterpret_cast<uint2*>(orow + 32 * j + 8 * q) =
-                    make_uint2(pack_bf16x2(acc[m][j][4 * q], acc[m][j][4 * q + 1]),
-                               pack_bf16x2(acc[m][j][4 * q + 2], acc[m][j][4 * q + 3]));
+            for (int e = 0; e < 4; ++e) {
+              const float gv = acc[m][0][4 * q + e], uv = acc[m][1][4 * q + e];
+              h[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
             }
+            *reinterpret_cast<uint2*>(orow + 8 * q) =
+                make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              *reinterpret_cast<uint2*>(orow + 32 * j + 8 * q) =
+                  make_uint2(pack_bf16x2(acc[m][j][4 * q], acc[m][j][4 * q + 1]),
+                             pack_bf16x2(acc[m][j][4 * q + 2], acc[m][j][4 * q + 3]));
           }
         }
       }
-    });
+    }
+    cur = nxt;
+    ocur = onxt;
   }
+  stream_finish();
 }
 
 int persistent_grid() {
@@ -241,13 +293,13 @@ template <int MODE>
 hipError_t launch_tiles(const GemmArgs& a, const moe_shape& s, hipStream_t st) {
   const int mean_rows = (s.T * s.k) / s.E;
   if (mean_rows >= 96)
-    grouped_gemm_kernel<MODE, 192, 4><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 160><<<persistent_grid(), kThreads, 0, st>>>(a);
   else if (mean_rows >= 48)
-    grouped_gemm_kernel<MODE, 128, 4><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 128><<<persistent_grid(), kThreads, 0, st>>>(a);
   else if (mean_rows >= 24)
-    grouped_gemm_kernel<MODE, 64, 4><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 64><<<persistent_grid(), kThreads, 0, st>>>(a);
   else
-    grouped_gemm_kernel<MODE, 32, 4><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 32><<<persistent_grid(), kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -63,6 +63,8 @@ def _route(L, shape, ptr=16 * 1024):
     (dict(D=2000), binding.MOE_ERR_UNSUPPORTED),
     (dict(F=500), binding.MOE_ERR_UNSUPPORTED),
     (dict(Fs=100), binding.MOE_ERR_UNSUPPORTED),
+    (dict(F=384), binding.MOE_ERR_UNSUPPORTED),
+    (dict(T=1200000), binding.MOE_ERR_UNSUPPORTED),
     (dict(T=1 << 28), binding.MOE_ERR_UNSUPPORTED),
 ])
 def test_bad_shapes_are_rejected_before_launch(L, kw, status):

@@ -19,7 +19,7 @@ from tests.gpu_common import (StackedInputs, assert_close_rel, check_routing, ou
 pytestmark = pytest.mark.gpu
 
 SMALL_BF16 = configs.variant(configs.XS2_T4096, name="small_bf16_t300", T=300, D=256, E=16, k=4,
-                             F=128, Fs=128)
+                             F=256, Fs=256)
 
 
 def full_parity(s, inp=None, gather=False):
@@ -102,7 +102,7 @@ EDGE = {
     "E1_k1": dict(E=1, k=1),
     "no_shared": dict(Fs=0),
     "T1": dict(T=1),
-    "T33_wide_shared": dict(T=33, Fs=256),
+    "T33_wide_shared": dict(T=33, Fs=512),
     "E256_T70": dict(T=70, E=256, k=8),
 }
 
