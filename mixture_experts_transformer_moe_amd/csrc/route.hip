@@ -2,17 +2,21 @@
 // weights ("Laguna M.1/XS.2 Technical Report", Key claims: sigmoid router,
 // token-choice top-8 of 256, post-top-k normalization; report section 3.1).
 //
-// bf16 path: one workgroup of 4 waves per 32 tokens.  Wave w owns experts
-// [64w, 64w+64) and accumulates the 32 x 64 logit block with
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulation) in the shared pipelined loop
-// (mma_pipeline.h): token rows and router-weight rows (hot in L2) stream into
-// LDS through a ring of direct global->LDS loads.  The bias is added once,
-// the fp32 logits are stored, and the same values are staged in LDS for the
-// selection.
-//
-// Selection: one wave per token, k rounds of a DPP wave maximum over an
-// order-preserving uint32 image of the logits, ties resolved to the lower
-// expert index by ballots; exact and independent of timing.
+// Two kernels.
+//   logits  bf16: one workgroup of 4 waves per 32 tokens; wave w owns experts
+//           [64w, 64w+64) and accumulates the 32 x 64 logit block with
+//           v_mfma_f32_32x32x16_bf16 (fp32 accumulation) in the shared
+//           pipelined loop (mma_pipeline.h): token rows and router-weight
+//           rows (hot in L2) stream into LDS through a ring of direct
+//           global->LDS loads.  The bias is added once and the fp32 logits
+//           stored.  fp32: one wave per token, plain fp32 FMA in index order.
+//   top-k   one 16-lane DPP row per token (4 tokens per wave); lane c holds
+//           the candidates e = c + 16 i.  Each of the k rounds takes the
+//           largest key among the candidates not yet taken (row maximum over
+//           an order-preserving uint32 image of z), then the lowest index
+//           holding it (row minimum), so the order is (z descending, index
+//           ascending) exactly and independent of timing.  Sigmoid of the
+//           selected logits, renormalised over the k slots.
 #include "mma_pipeline.h"
 
 namespace moe {
@@ -29,60 +33,77 @@ __device__ __forceinline__ uint32_t order_key(float z) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Maximum of v over the wave: DPP shifts inside each row of 16 lanes, then the
-// four row maxima through readlane.  The result is wave-uniform.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+// Row-wide (16 lanes) reductions through DPP row shifts: after them lane 15
+// of each row holds the row's result, read back by readlane and handed to
+// every lane of the row.  `id` is the identity of the operation.
+template <typename Op>
+__device__ __forceinline__ uint32_t row_reduce_u32(uint32_t v, uint32_t id, Op op) {
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(v), 0x118, 0xf, 0xf, false)));
   const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
   const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
-  return max(max(r0, r1), max(r2, r3));
+  const int row = (threadIdx.x & 63) >> 4;
+  return row == 0 ? r0 : row == 1 ? r1 : row == 2 ? r2 : r3;
 }
 
-// One wave selects the top-k of zrow[0..E) and writes slot order + weights.
-// Lane l holds candidates e = l + 64 i (i < 4).  Each round takes the largest
-// key among the candidates not yet taken (wave max), then the lowest index
-// holding it (ballots scanned in index order), so the order is (z descending,
-// index ascending) exactly, whatever the values (non-finite ones included).
-__device__ void wave_topk(const float* zrow, int E, int k, int32_t* idx_out, float* w_out) {
-  const int lane = threadIdx.x & 63;
-  uint32_t key[4];
-  uint32_t taken = 0;                       // bit i: candidate i taken or absent
+__device__ __forceinline__ float row_sum_f32(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));
+  const int b0 = __builtin_amdgcn_readlane(__float_as_int(v), 15), b1 = __builtin_amdgcn_readlane(__float_as_int(v), 31);
+  const int b2 = __builtin_amdgcn_readlane(__float_as_int(v), 47), b3 = __builtin_amdgcn_readlane(__float_as_int(v), 63);
+  const int row = (threadIdx.x & 63) >> 4;
+  return __int_as_float(row == 0 ? b0 : row == 1 ? b1 : row == 2 ? b2 : b3);
+}
+
+constexpr int kTopkThreads = 256;              // 4 waves x 4 tokens
+constexpr int kTopkTokens = kTopkThreads / 16;
+
+// Top-k of the stored logits, 16 lanes per token (E <= 256, k <= 16).
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ logits,
+                                                            int32_t* __restrict__ idx,
+                                                            float* __restrict__ wout, int T, int E, int k) {
+  const int c = threadIdx.x & 15;
+  const int t_raw = blockIdx.x * kTopkTokens + (threadIdx.x >> 4);
+  const int t = min(t_raw, T - 1);                 // rows past T compute a copy of the last one
+  const float* z = logits + static_cast<size_t>(t) * E;
+  uint32_t key[16];
+  uint32_t taken = 0;                              // bit i: candidate c + 16 i taken or absent
+  // all 16 loads unconditional (clamped index), so that they are in flight
+  // together
+  float zv[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? order_key(zrow[e]) : 0u;
+  for (int i = 0; i < 16; ++i) zv[i] = z[min(c + 16 * i, E - 1)];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = c + 16 * i;
+    key[i] = e < E ? order_key(zv[i]) : 0u;        // real keys are >= 1
     if (e >= E) taken |= 1u << i;
   }
   int my_e = 0;
   for (int j = 0; j < k; ++j) {
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 16; ++i)
       if (!((taken >> i) & 1u)) m = max(m, key[i]);
-    const uint32_t best = wave_max_u32(m);
-    int e = 0;
-    bool found = false;
+    const uint32_t best = row_reduce_u32(m, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+    uint32_t cand = 0xffffu;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const unsigned long long b = __ballot(!((taken >> i) & 1u) && key[i] == best);
-      if (!found && b != 0ull) {
-        e = 64 * i + __ffsll(b) - 1;
-        found = true;
-      }
-    }
-    if ((e & 63) == lane) taken |= 1u << (e >> 6);
-    if (lane == j) my_e = e;
+    for (int i = 15; i >= 0; --i)
+      if (!((taken >> i) & 1u) && key[i] == best) cand = static_cast<uint32_t>(c + 16 * i);
+    const int e = static_cast<int>(row_reduce_u32(cand, 0xffffu, [](uint32_t a, uint32_t b) { return min(a, b); }));
+    if ((e & 15) == c) taken |= 1u << (e >> 4);
+    if (c == j) my_e = e;
   }
-  float s = 0.f;
-  if (lane < k) s = 1.0f / (1.0f + expf(-zrow[my_e]));
-  float sum = 0.f;
-  for (int j = 0; j < k; ++j) sum += __shfl(s, j, 64);    // slot order
-  if (lane < k) {
-    idx_out[lane] = my_e;
-    w_out[lane] = s / sum;
+  // sigmoid of the selected logits (exact fp32 values), renormalised
+  const float s = c < k ? 1.0f / (1.0f + expf(-z[my_e])) : 0.f;
+  const float sum = row_sum_f32(s);
+  if (t_raw < T && c < k) {
+    idx[static_cast<size_t>(t) * k + c] = my_e;
+    wout[static_cast<size_t>(t) * k + c] = s / sum;
   }
 }
 
@@ -90,13 +111,10 @@ template <int NS>
 __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __restrict__ x,
                                                             const bf16_t* __restrict__ wr,
                                                             const float* __restrict__ bias,
-                                                            float* __restrict__ logits,
-                                                            int32_t* __restrict__ idx,
-                                                            float* __restrict__ wout, int T, int D,
-                                                            int E, int k) {
+                                                            float* __restrict__ logits, int T, int D,
+                                                            int E) {
   using PT = PipeTile<kRouteTokens, kMaxE>;
   constexpr int kLdsElems = NS * PT::kStageElems;
-  static_assert(kRouteTokens * (kMaxE + 1) * 2 <= kLdsElems, "logit tile fits the ring");
   __shared__ __attribute__((aligned(16))) bf16_t lds[kLdsElems];
   const int t0 = blockIdx.x * kRouteTokens;
   const int tid = threadIdx.x;
@@ -111,7 +129,6 @@ __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __rest
       a_src, b_src, [&](int r) { return x + static_cast<size_t>(min(t0 + r, T - 1)) * D; },
       [&](int r) { return wr + static_cast<size_t>(min(r, E - 1)) * D; });
   const int brow[2] = {e_base, e_base + 32};
-  float (*zs)[kMaxE + 1] = reinterpret_cast<float (*)[kMaxE + 1]>(lds);
   mma_pipeline<kRouteTokens, kMaxE, NS>(a_src, b_src, D / kPipeBK, valid, brow, lds, [&](auto& acc) {
     // lane: token (lane & 31); register quad q: experts e0 + 8 q + 4 (lane / 32) + 0..3
     const int row = lane & 31;
@@ -124,7 +141,6 @@ __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __rest
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           z[c] = acc[0][j][4 * q + c] + ((bias && e0 + c < E) ? bias[e0 + c] : 0.f);
-          zs[row][e0 + c] = z[c];
         }
         if (row < valid && e0 < E) {
           float* dst = logits + static_cast<size_t>(t0 + row) * E + e0;
@@ -137,22 +153,13 @@ __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __rest
       }
     }
   });
-  __syncthreads();
-  for (int r = wave; r < kRouteTokens; r += 4) {
-    const int t = t0 + r;
-    if (t < T) wave_topk(zs[r], E, k, idx + static_cast<size_t>(t) * k, wout + static_cast<size_t>(t) * k);
-  }
 }
 
 // fp32 path: one wave per token, logits by plain fp32 FMA in index order.
 __global__ __launch_bounds__(64) void route_f32_kernel(const float* __restrict__ x,
                                                        const float* __restrict__ wr,
                                                        const float* __restrict__ bias,
-                                                       float* __restrict__ logits,
-                                                       int32_t* __restrict__ idx,
-                                                       float* __restrict__ wout, int T, int D,
-                                                       int E, int k) {
-  __shared__ float zs[kMaxE];
+                                                       float* __restrict__ logits, int T, int D, int E) {
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
   const float* xr = x + static_cast<size_t>(t) * D;
@@ -160,29 +167,33 @@ __global__ __launch_bounds__(64) void route_f32_kernel(const float* __restrict__
     const float* w = wr + static_cast<size_t>(e) * D;
     float acc = 0.f;
     for (int d = 0; d < D; ++d) acc = fmaf(xr[d], w[d], acc);
-    const float z = acc + (bias ? bias[e] : 0.f);
-    zs[e] = z;
-    logits[static_cast<size_t>(t) * E + e] = z;
+    logits[static_cast<size_t>(t) * E + e] = acc + (bias ? bias[e] : 0.f);
   }
-  __syncthreads();
-  wave_topk(zs, E, k, idx + static_cast<size_t>(t) * k, wout + static_cast<size_t>(t) * k);
 }
 
 }  // namespace
+
+hipError_t launch_topk(const moe_shape& s, const float* logits, int32_t* idx, float* w, hipStream_t st) {
+  const int blocks = (s.T + kTopkTokens - 1) / kTopkTokens;
+  topk_kernel<<<blocks, kTopkThreads, 0, st>>>(logits, idx, w, s.T, s.E, s.k);
+  return hipGetLastError();
+}
 
 hipError_t launch_route_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* wr,
                              const float* bias, float* logits, int32_t* idx, float* w,
                              hipStream_t st) {
   const int blocks = (s.T + kRouteTokens - 1) / kRouteTokens;
-  route_bf16_kernel<4><<<blocks, 256, 0, st>>>(x, wr, bias, logits, idx, w, s.T, s.D, s.E, s.k);
-  return hipGetLastError();
+  route_bf16_kernel<4><<<blocks, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
+  if (hipError_t e = hipGetLastError()) return e;
+  return launch_topk(s, logits, idx, w, st);
 }
 
 hipError_t launch_route_f32(const moe_shape& s, const float* x, const float* wr,
                             const float* bias, float* logits, int32_t* idx, float* w,
                             hipStream_t st) {
-  route_f32_kernel<<<s.T, 64, 0, st>>>(x, wr, bias, logits, idx, w, s.T, s.D, s.E, s.k);
-  return hipGetLastError();
+  route_f32_kernel<<<s.T, 64, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
+  if (hipError_t e = hipGetLastError()) return e;
+  return launch_topk(s, logits, idx, w, st);
 }
 
 }  // namespace moe
