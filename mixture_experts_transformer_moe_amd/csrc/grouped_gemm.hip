@@ -65,12 +65,16 @@ struct TileOut {
 // (mma_stream.h).  Wave w holds the gate block and the up block of the same 32
 // columns, so SwiGLU is applied in registers; outputs go straight from
 // registers to memory, four adjacent bf16 values (8 bytes) per lane and store.
-template <int MODE, int BM>
+template <int MODE, int BM, int NB, int PF>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
-  using ST = StreamTile<BM>;
+  using ST = StreamTile<BM, NB, PF>;
   constexpr int MBW = ST::MBW;
-  constexpr int kOutCols = (MODE == kGateUp) ? 128 : 256;       // output columns per tile
+  // output columns per tile: gate_up pairs NB / 2 gate blocks with the up
+  // blocks of the same columns (32 NB / 2 columns per wave); down: 32 NB per wave
+  constexpr int kWaveCols = (MODE == kGateUp) ? 16 * NB : 32 * NB;
+  constexpr int kOutCols = 4 * kWaveCols;
   __shared__ __attribute__((aligned(16))) bf16_t lds[kStreamNS * ST::kAElems];
+  static_assert(kStreamNS * ST::kAElems * 2 + 2 * (kMaxE + 1) * 4 <= 160 * 1024, "LDS");
   __shared__ int tile_end[kMaxE + 1];
   __shared__ int row_base[kMaxE + 1];
   __shared__ int shared_bm;
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   const int lane = tid & 63;
 
   // ---- sources and output of tile ti (all but the token-row offsets uniform)
-  auto decode = [&](int ti, StreamSrc<BM>& src, TileOut& o) {
+  auto decode = [&](int ti, StreamSrc<BM, NB>& src, TileOut& o) {
     int lo = 0, hi = E;                     // group: first with tile_end > ti
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -157,7 +161,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     const int Nout = shared ? g.Ns : g.N;
     const int n0 = n_tile * kOutCols;
     const int valid = min(bm, M - m0);
-    src.groups = (valid + 31) >> 5;
     src.nkb = K / kStreamBK;
 
     // token rows: lane's chunk of LDS load q is row 8 (MBW wave + q) + lane / 8
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int q = 0; q < MBW; ++q) {
       int row, col;
-      chunk_source(stream_a_slot<BM>(q, wave, lane), row, col);
+      chunk_source(stream_a_slot<MBW>(q, wave, lane), row, col);
       uint32_t r;
       if (gathered) {
         int tok;
@@ -208,33 +211,31 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     const bf16_t* wbase =
         shared ? g.w_shared
                : g.w_routed + static_cast<size_t>(grp) * packed_matrix_elems(MODE == kGateUp ? 2 * Nout : Nout, K);
-    int wrow0, wrow1, col0;
-    if (MODE == kGateUp) {           // gate block and the up block of the same 32 columns
-      wrow0 = n0 + 32 * wave;
-      wrow1 = Nout + n0 + 32 * wave;
-      col0 = n0 + 32 * wave;
-    } else {
-      wrow0 = n0 + 64 * wave;
-      wrow1 = n0 + 64 * wave + 32;
-      col0 = n0 + 64 * wave;
+    // the wave's weight block rows and its first output column
+    const int col0 = n0 + kWaveCols * wave;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      // gate_up: blocks j < NB / 2 are gate rows, the others the up rows of
+      // the same columns; down: NB consecutive blocks
+      const int wrow = MODE == kGateUp ? (j < NB / 2 ? col0 + 32 * j : Nout + col0 + 32 * (j - NB / 2))
+                                       : col0 + 32 * j;
+      src.w[j] = wbase + static_cast<size_t>(wrow >> 5) * (K >> 4) * 512;
     }
-    src.w[0] = wbase + static_cast<size_t>(wrow0 >> 5) * (K >> 4) * 512;
-    src.w[1] = wbase + static_cast<size_t>(wrow1 >> 5) * (K >> 4) * 512;
     o.out = (shared ? g.out_shared + static_cast<size_t>(m0) * Nout
                     : g.out_routed + static_cast<size_t>(rb + m0) * Nout) + col0;
     o.ld = Nout;
     o.valid = valid;
   };
 
-  StreamSrc<BM> cur, nxt;
+  StreamSrc<BM, NB> cur, nxt;
   TileOut ocur, onxt;
-  StreamState ss;
+  StreamState<NB, PF> ss;
   decode(pos, cur, ocur);
-  stream_start<BM>(cur, ss, lds);
+  stream_start<BM, NB, PF>(cur, ss, lds);
   for (int ti = pos; ti < total; ti += G) {
     const TileOut o = ocur;
-    f32x16 acc[MBW][2];
-    stream_tile<BM>(cur, nxt, [&]() {
+    f32x16 acc[MBW][NB];
+    stream_tile<BM, NB, PF>(cur, nxt, [&]() {
       if (ti + G >= total) return false;
       decode(ti + G, nxt, onxt);
       return true;
@@ -249,23 +250,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {            // registers 4q..4q+3: 4 adjacent columns
           if (MODE == kGateUp) {
-            float h[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float gv = acc[m][0][4 * q + e], uv = acc[m][1][4 * q + e];
-              h[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+            for (int j = 0; j < NB / 2; ++j) {
+              float h[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float gv = acc[m][j][4 * q + e], uv = acc[m][j + NB / 2][4 * q + e];
+                h[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+              }
+              *reinterpret_cast<uint2*>(orow + 32 * j + 8 * q) =
+                  make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
             }
-            *reinterpret_cast<uint2*>(orow + 8 * q) =
-                make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
           } else {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NB; ++j)
               *reinterpret_cast<uint2*>(orow + 32 * j + 8 * q) =
                   make_uint2(pack_bf16x2(acc[m][j][4 * q], acc[m][j][4 * q + 1]),
                              pack_bf16x2(acc[m][j][4 * q + 2], acc[m][j][4 * q + 3]));
           }
         }
       }
+      // one token block at a time: reading every accumulator out at once
+      // would need as many VGPRs, on top of the weight ring in flight
+      __builtin_amdgcn_sched_barrier(0);
     }
     cur = nxt;
     ocur = onxt;
@@ -287,19 +294,28 @@ int persistent_grid() {
   return grid;
 }
 
-// Row-block height by the mean rows per expert (k*T/E): tall tiles when experts
-// hold many rows (fewer weight re-reads), short ones for decode-sized batches.
+// Tile shape by the mean rows per expert (k*T/E).  Up to ~200 rows the weight
+// stream from HBM is the limit: tall row blocks (an expert's rows mostly fit
+// one, so its weights stream once), 2 weight blocks per wave and a deep weight
+// prefetch (16 steps); shorter blocks for decode-sized batches.  Beyond that
+// MFMA issue, LDS reads and the L2 traffic of re-read weights compete: 96-row
+// blocks with 4 weight blocks per wave (each A fragment read from LDS feeds 4
+// MFMAs) measured best among the shapes whose accumulators and weight ring fit
+// the registers, when the output width allows their wider tiles.
 template <int MODE>
 hipError_t launch_tiles(const GemmArgs& a, const moe_shape& s, hipStream_t st) {
   const int mean_rows = (s.T * s.k) / s.E;
-  if (mean_rows >= 96)
-    grouped_gemm_kernel<MODE, 160><<<persistent_grid(), kThreads, 0, st>>>(a);
+  const int wide = MODE == kGateUp ? 256 : 512;            // output columns of an NB = 4 tile
+  if (mean_rows >= 192 && a.N % wide == 0 && (!a.has_shared || a.Ns % wide == 0))
+    grouped_gemm_kernel<MODE, 96, 4, 8><<<persistent_grid(), kThreads, 0, st>>>(a);
+  else if (mean_rows >= 96)
+    grouped_gemm_kernel<MODE, 160, 2, 16><<<persistent_grid(), kThreads, 0, st>>>(a);
   else if (mean_rows >= 48)
-    grouped_gemm_kernel<MODE, 128><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 128, 2, 16><<<persistent_grid(), kThreads, 0, st>>>(a);
   else if (mean_rows >= 24)
-    grouped_gemm_kernel<MODE, 64><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 64, 2, 16><<<persistent_grid(), kThreads, 0, st>>>(a);
   else
-    grouped_gemm_kernel<MODE, 32><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 32, 2, 16><<<persistent_grid(), kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

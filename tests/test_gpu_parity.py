@@ -33,8 +33,9 @@ def full_parity(s, inp=None, gather=False):
 
 
 def sampled_parity(s, n_tokens=40, seed=0):
+    # the benchmark's launch configuration: the first GEMM gathers token rows
     inp = StackedInputs(LayerInputs(s))
-    x, w, b = run_layer(s, inp)
+    x, w, b = run_layer(s, inp, gather=True)
     r = check_routing(s, inp, b)
     rng = np.random.default_rng(seed)
     toks = set(rng.choice(s.T, size=min(n_tokens, s.T), replace=False).tolist()) | {0, s.T - 1}
@@ -104,6 +105,11 @@ EDGE = {
     "T1": dict(T=1),
     "T33_wide_shared": dict(T=33, Fs=512),
     "E256_T70": dict(T=70, E=256, k=8),
+    # tile shapes chosen by the mean rows per expert (k T / E)
+    "rows37_T300_E32": dict(T=300, E=32, k=4),
+    "rows150_T600_E32": dict(T=600, E=32, k=8),
+    "rows256_T512_D512": dict(T=512, D=512, E=16, k=8),
+    "rows350_T700_D512": dict(T=700, D=512, E=16, k=8, Fs=512),
 }
 
 
@@ -111,6 +117,13 @@ EDGE = {
 def test_edge_shapes_bf16(case):
     s = configs.variant(SMALL_BF16, name=f"edge_{case}", **EDGE[case])
     full_parity(s)
+
+
+@pytest.mark.parametrize("case", ["rows150_T600_E32", "rows256_T512_D512", "rows350_T700_D512", "T1",
+                                  "E256_T70"])
+def test_edge_shapes_bf16_gathered(case):
+    s = configs.variant(SMALL_BF16, name=f"edge_gather_{case}", **EDGE[case])
+    full_parity(s, gather=True)
 
 
 @pytest.mark.parametrize("case", ["k1", "no_shared", "T1", "k_eq_E"])
