@@ -46,7 +46,7 @@ PEAK_F32_TFLOPS = 157.3
 # the traffic is reported as null until the counters are taken again.
 FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
-GEMM_SOURCES = ("grouped_gemm.hip", "mma_stream.h", "mma_pipeline.h", "moe_internal.h")
+GEMM_SOURCES = ("grouped_gemm.hip", "mma_stream.h", "lds_dma.h", "moe_internal.h")
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
     "xs2_bf16_t4096_d2048": (628393.3, 36864.5,

@@ -36,7 +36,7 @@
 
 #include <type_traits>
 
-#include "mma_pipeline.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -85,6 +85,12 @@ struct StreamSrc {
   int nkb;                              // K / 64, a multiple of 4
 };
 
+// Weight operand of block j for 16-wide K step `step`.
+template <int BM, int NB>
+__device__ __forceinline__ const bf16_t* stream_wstep(const StreamSrc<BM, NB>& s, int j, int step) {
+  return s.w[j] + step * 512;
+}
+
 // What stays in flight between tiles.
 template <int NB, int PF>
 struct StreamState {
@@ -118,7 +124,7 @@ __device__ __forceinline__ void stream_start(const StreamSrc<BM, NB>& s, StreamS
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) ss.bq[p][j] = *reinterpret_cast<const u32x4*>(s.w[j] + p * 512 + lane * 8);
+    for (int j = 0; j < NB; ++j) ss.bq[p][j] = *reinterpret_cast<const u32x4*>(stream_wstep(s, j, p) + lane * 8);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -182,16 +188,11 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
   static_assert(kKeep < 64, "vmcnt range");
   const int lane = threadIdx.x & 63;
   const int NKB = cur.nkb;
-  const int NKS = 4 * NKB;
 #pragma unroll
   for (int m = 0; m < MBW; ++m)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[m][j] = f32x16{0.f};
   bool has_next = false;
-  const bf16_t* tail_w[NB];
-  int tail_stride = 0;
-#pragma unroll
-  for (int j = 0; j < NB; ++j) tail_w[j] = cur.w[j];
 
   // u: position of the block in its unrolled group (ring slots 4u..4u+3 mod PF)
   auto kblock = [&](int kb, auto u_tag, auto last_tag) {
@@ -227,11 +228,13 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
       stream_step<MBW, NB>(As, ch, ss.bq[slot], acc);
       // the step PF ahead: this tile's, or in the last blocks past its end the
       // next tile's (every tile has at least 16 steps)
+      // (after the last tile: a repeat of any step of this one)
       const bool from_next = last && (4 * u + i + PF >= 16);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const bf16_t* src = from_next ? tail_w[j] + (4 * u + i + PF - 16) * tail_stride
-                                      : cur.w[j] + (4 * kb + i + PF) * 512;
+        const bf16_t* src = !from_next ? stream_wstep(cur, j, 4 * kb + i + PF)
+                            : has_next ? stream_wstep(nxt, j, 4 * u + i + PF - 16)
+                                       : cur.w[j];
         ss.bq[slot][j] = *reinterpret_cast<const u32x4*>(src + lane * 8);
       }
       // keep each refill right after the step that frees its registers: the
@@ -255,12 +258,7 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
       kblock(kb + 3, I3{}, No{});
     }
   }
-  // weight source of refills past this tile's last step: the next tile's first
-  // steps, or (last tile) a repeat of this tile's last step
   has_next = next();
-#pragma unroll
-  for (int j = 0; j < NB; ++j) tail_w[j] = has_next ? nxt.w[j] : cur.w[j] + (NKS - 1) * 512;
-  tail_stride = has_next ? 512 : 0;
   kblock(kb, I0{}, Yes{});
   kblock(kb + 1, I1{}, Yes{});
   kblock(kb + 2, I2{}, Yes{});

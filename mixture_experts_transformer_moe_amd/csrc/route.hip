@@ -3,13 +3,9 @@
 // token-choice top-8 of 256, post-top-k normalization; report section 3.1).
 //
 // Two kernels.
-//   logits  bf16: one workgroup of 4 waves per 32 tokens; wave w owns experts
-//           [64w, 64w+64) and accumulates the 32 x 64 logit block with
-//           v_mfma_f32_32x32x16_bf16 (fp32 accumulation) in the shared
-//           pipelined loop (mma_pipeline.h): token rows and router-weight
-//           rows (hot in L2) stream into LDS through a ring of direct
-//           global->LDS loads.  The bias is added once and the fp32 logits
-//           stored.  fp32: one wave per token, plain fp32 FMA in index order.
+//   logits  bf16: blocks of tokens x experts on MFMA, fp32 accumulation, the
+//           bias added once, fp32 logits stored (route_bf16_kernel below).
+//           fp32: one wave per token, plain fp32 FMA in index order.
 //   top-k   one 16-lane DPP row per token (4 tokens per wave); lane c holds
 //           the candidates e = c + 16 i.  Each of the k rounds takes the
 //           largest key among the candidates not yet taken (row maximum over
@@ -17,13 +13,11 @@
 //           holding it (row minimum), so the order is (z descending, index
 //           ascending) exactly and independent of timing.  Sigmoid of the
 //           selected logits, renormalised over the k slots.
-#include "mma_pipeline.h"
+#include "lds_dma.h"
 
 namespace moe {
 namespace {
 
-constexpr int kRouteTokens = 32;
-constexpr int kMaxE = 256;
 
 // Monotone map of fp32 onto uint32 (larger z -> larger key); -0.0 is folded
 // onto +0.0 first so that the two zeros tie.
@@ -107,52 +101,131 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
 }
 
-template <int NS>
+// Router logits, bf16: a workgroup of 4 waves computes a TM x TN block of
+// logits (tokens x experts) over the whole of D.  Wave w sits at (tm, tn, ks):
+// it owns the 32 x 32 block (tm, tn) and, when the four waves split K (KS = 4
+// for small batches, so that few tokens still keep 4 load streams per CU),
+// the K blocks ks, ks + KS, ...; the partial blocks are summed in LDS in ks
+// order.  Token rows and router rows reach LDS by direct global->LDS loads
+// (each covers 8 rows x 128 bytes, XOR-swizzled) through a ring of NS stages
+// of KS 64-wide K blocks, the same number of loads per wave in every stage, so
+// every wait is a constant.  v_mfma_f32_32x32x16_bf16 with the router rows as the first
+// operand: lane l holds token (l mod 32), register quads 4 adjacent experts.
+template <int TM, int TN, int KS, int NS>
 __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __restrict__ x,
                                                             const bf16_t* __restrict__ wr,
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ logits, int T, int D,
                                                             int E) {
-  using PT = PipeTile<kRouteTokens, kMaxE>;
-  constexpr int kLdsElems = NS * PT::kStageElems;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[kLdsElems];
-  const int t0 = blockIdx.x * kRouteTokens;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int e_base = 64 * wave;
-  const int valid = min(kRouteTokens, T - t0);
+  constexpr int kRows = TM + TN;                       // rows per K block: tokens, then experts
+  constexpr int kBlockElems = kRows * kPipeBK;
+  constexpr int kStageElems = KS * kBlockElems;
+  constexpr int kLoads = KS * kRows / 8;               // 1 KB loads per stage
+  constexpr int LPW = kLoads / 4;                      // per wave
+  static_assert((TM / 32) * (TN / 32) * KS == 4 && kLoads % 4 == 0, "4 waves, equal loads per stage");
+  static_assert(NS * kStageElems * 2 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) bf16_t lds[NS * kStageElems];
+  const int tiles_n = (E + TN - 1) / TN;
+  const int t0 = (blockIdx.x / tiles_n) * TM;
+  const int e0 = (blockIdx.x % tiles_n) * TN;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int ks = wave % KS;
+  const int tm = (wave / KS) % (TM / 32);
+  const int tn = (wave / KS) / (TM / 32);
+  const int NKB = D / kPipeBK;                         // a multiple of KS
 
-  const bf16_t* a_src[PT::kAGroups];
-  const bf16_t* b_src[PT::kBInst];
-  pipe_sources<kRouteTokens, kMaxE>(
-      a_src, b_src, [&](int r) { return x + static_cast<size_t>(min(t0 + r, T - 1)) * D; },
-      [&](int r) { return wr + static_cast<size_t>(min(r, E - 1)) * D; });
-  const int brow[2] = {e_base, e_base + 32};
-  mma_pipeline<kRouteTokens, kMaxE, NS>(a_src, b_src, D / kPipeBK, valid, brow, lds, [&](auto& acc) {
-    // lane: token (lane & 31); register quad q: experts e0 + 8 q + 4 (lane / 32) + 0..3
-    const int row = lane & 31;
+  // this lane's LPW loads per stage: load q of wave w is load i = LPW w + q of
+  // the stage: K block i / (kRows / 8), rows 8 (i mod (kRows / 8)) + 0..7 of it
+  const bf16_t* src[LPW];
+  uint32_t dst_off[LPW];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+  for (int q = 0; q < LPW; ++q) {
+    const int i = LPW * wave + q;
+    const int kb = i / (kRows / 8);
+    const int P = (i % (kRows / 8)) * 64 + lane;       // chunk slot inside the K block
+    int row, col;
+    chunk_source(P, row, col);
+    const bf16_t* r = row < TM ? x + static_cast<size_t>(min(t0 + row, T - 1)) * D
+                               : wr + static_cast<size_t>(min(e0 + row - TM, E - 1)) * D;
+    src[q] = r + kb * kPipeBK + col;
+    dst_off[q] = static_cast<uint32_t>((kb * kBlockElems + (i % (kRows / 8)) * 512) * 2);
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  // stage s holds K blocks s KS .. s KS + KS - 1
+  const int nst = NKB / KS;
+  // workgroups that share router rows start at different K offsets, so that
+  // they do not all ask the same L2 lines for the same block at once (each
+  // token's sum is still taken in one fixed order)
+  const int rot = (blockIdx.x / tiles_n) % nst;
+  auto issue = [&](int slot, int s) {
+    const uint32_t base = lds0 + static_cast<uint32_t>(slot * kStageElems * 2);
+    const int sr = s + rot < nst ? s + rot : s + rot - nst;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e0 = e_base + 32 * j + 8 * q + 4 * (lane >> 5);
-        float z[4];
+    for (int q = 0; q < LPW; ++q)
+      dma16(src[q] + static_cast<size_t>(sr) * KS * kPipeBK, __builtin_amdgcn_readfirstlane(base + dst_off[q]));
+  };
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          z[c] = acc[0][j][4 * q + c] + ((bias && e0 + c < E) ? bias[e0 + c] : 0.f);
-        }
-        if (row < valid && e0 < E) {
-          float* dst = logits + static_cast<size_t>(t0 + row) * E + e0;
-          if (e0 + 4 <= E && (E & 3) == 0) {
-            *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
-          } else {
-            for (int c = 0; c < 4 && e0 + c < E; ++c) dst[c] = z[c];
-          }
-        }
-      }
+  for (int s = 0; s < NS - 1; ++s) issue(s, min(s, nst - 1));
+
+  f32x16 acc = f32x16{0.f};
+  const int arow = 32 * tm + (lane & 31);
+  const int brow = TM + 32 * tn + (lane & 31);
+  int slot = 0;
+  for (int s = 0; s < nst; ++s) {
+    // this stage was issued NS - 1 stages ago; the NS - 2 later ones (LPW
+    // loads each) may still be in flight
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(LPW * (NS - 2)));
+    __builtin_amdgcn_s_barrier();
+    issue(slot == 0 ? NS - 1 : slot - 1, min(s + NS - 1, nst - 1));
+    const bf16_t* blk = lds + slot * kStageElems + ks * kBlockElems;
+    // all fragments of the block first: one LDS latency per block, not per step
+    bf16x8 fa[4], fb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = 2 * i + (lane >> 5);
+      fb[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&blk[pipe_swz(brow, ch)]));
+      fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&blk[pipe_swz(arow, ch)]));
     }
-  });
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[i], acc, 0, 0, 0);
+    slot = slot + 1 == NS ? 0 : slot + 1;
+  }
+  // the tail loads (clamped repeats) land before LDS is reused or the
+  // workgroup ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  if constexpr (KS > 1) {
+    __builtin_amdgcn_s_barrier();
+    float* red = reinterpret_cast<float*>(lds);        // [KS][16][64]
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(ks * 16 + r) * 64 + lane] = acc[r];
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = red[r * 64 + lane];
+#pragma unroll
+      for (int j = 1; j < KS; ++j) v += red[(j * 16 + r) * 64 + lane];
+      acc[r] = v;
+    }
+  }
+  const int t = t0 + 32 * tm + (lane & 31);
+  if (t >= T) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = e0 + 32 * tn + mfma32_row(4 * q, lane);   // 4 adjacent experts
+    float z[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) z[c] = acc[4 * q + c] + ((bias && e + c < E) ? bias[min(e + c, E - 1)] : 0.f);
+    float* dst = logits + static_cast<size_t>(t) * E + e;
+    if ((E & 3) == 0 && e + 4 <= E) {
+      *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
+    } else {
+      for (int c = 0; c < 4; ++c)
+        if (e + c < E) dst[c] = z[c];
+    }
+  }
 }
 
 // fp32 path: one wave per token, logits by plain fp32 FMA in index order.
@@ -182,8 +255,15 @@ hipError_t launch_topk(const moe_shape& s, const float* logits, int32_t* idx, fl
 hipError_t launch_route_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* wr,
                              const float* bias, float* logits, int32_t* idx, float* w,
                              hipStream_t st) {
-  const int blocks = (s.T + kRouteTokens - 1) / kRouteTokens;
-  route_bf16_kernel<4><<<blocks, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
+  // 64 x 64 blocks when they are enough to fill the chip, else 32 x 32 blocks
+  // with the K split over the workgroup's waves
+  const int big = ((s.T + 63) / 64) * ((s.E + 63) / 64);
+  if (big >= 128) {
+    route_bf16_kernel<64, 64, 1, 8><<<big, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
+  } else {
+    const int blocks = ((s.T + 31) / 32) * ((s.E + 31) / 32);
+    route_bf16_kernel<32, 32, 4, 4><<<blocks, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
+  }
   if (hipError_t e = hipGetLastError()) return e;
   return launch_topk(s, logits, idx, w, st);
 }
