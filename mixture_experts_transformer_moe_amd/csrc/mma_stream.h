@@ -193,6 +193,10 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[m][j] = f32x16{0.f};
   bool has_next = false;
+  const bf16_t* tail_w[NB];
+  int tail_stride = 0;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) tail_w[j] = cur.w[j];
 
   // u: position of the block in its unrolled group (ring slots 4u..4u+3 mod PF)
   auto kblock = [&](int kb, auto u_tag, auto last_tag) {
@@ -228,13 +232,11 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
       stream_step<MBW, NB>(As, ch, ss.bq[slot], acc);
       // the step PF ahead: this tile's, or in the last blocks past its end the
       // next tile's (every tile has at least 16 steps)
-      // (after the last tile: a repeat of any step of this one)
       const bool from_next = last && (4 * u + i + PF >= 16);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const bf16_t* src = !from_next ? stream_wstep(cur, j, 4 * kb + i + PF)
-                            : has_next ? stream_wstep(nxt, j, 4 * u + i + PF - 16)
-                                       : cur.w[j];
+        const bf16_t* src = from_next ? tail_w[j] + (4 * u + i + PF - 16) * tail_stride
+                                      : stream_wstep(cur, j, 4 * kb + i + PF);
         ss.bq[slot][j] = *reinterpret_cast<const u32x4*>(src + lane * 8);
       }
       // keep each refill right after the step that frees its registers: the
@@ -258,7 +260,12 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
       kblock(kb + 3, I3{}, No{});
     }
   }
+  // weight source of refills past this tile's last step: the next tile's first
+  // steps, or (last tile) a repeat of one step of this tile
   has_next = next();
+#pragma unroll
+  for (int j = 0; j < NB; ++j) tail_w[j] = has_next ? nxt.w[j] : cur.w[j];
+  tail_stride = has_next ? 512 : 0;
   kblock(kb, I0{}, Yes{});
   kblock(kb + 1, I1{}, Yes{});
   kblock(kb + 2, I2{}, Yes{});
