@@ -142,6 +142,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 
   // ---- sources and output of tile ti (all but the token-row offsets uniform)
   auto decode = [&](int ti, StreamSrc<BM, NB>& src, TileOut& o) {
+    // per-lane row / column arithmetic is redone here for every tile: hoisted
+    // out of the tile loop it would hold registers across the whole stream
+    int lane = tid & 63;
+    asm volatile("" : "+v"(lane));
     int lo = 0, hi = E;                     // group: first with tile_end > ti
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -268,11 +272,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
                   make_uint2(pack_bf16x2(acc[m][j][4 * q], acc[m][j][4 * q + 1]),
                              pack_bf16x2(acc[m][j][4 * q + 2], acc[m][j][4 * q + 3]));
           }
+          // a few accumulators at a time: reading them all out at once would
+          // need as many VGPRs, on top of the weight ring in flight
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // one token block at a time: reading every accumulator out at once
-      // would need as many VGPRs, on top of the weight ring in flight
-      __builtin_amdgcn_sched_barrier(0);
     }
     cur = nxt;
     ocur = onxt;

@@ -11,8 +11,8 @@
 //   * Weights are stored packed in MFMA fragment order (moe_pack_weights): the
 //     operand of one wave for one 32-row block and one 16-wide K step is 1 KB
 //     of contiguous memory, lane l holding 16 bytes.  Each wave streams its
-//     blocks with whole-line 16-byte loads into a ring of PF steps (8 or 16)
-//     of registers -- register space is far larger than LDS, so many bytes are in
+//     blocks with whole-line 16-byte loads into a ring of PF steps (4, 8 or
+//     16) of registers -- register space is far larger than LDS, so many bytes are in
 //     flight per CU, which is what an HBM-bound stream needs.
 //   * Token rows (gathered through the expert order, L2/MALL resident) move by
 //     direct global->LDS loads (global_load_lds_dwordx4) into a ring of NS
@@ -48,7 +48,8 @@ template <int BM, int NB, int PF>
 struct StreamTile {
   static constexpr int MBW = BM / 32;             // token blocks (every wave covers all)
   static constexpr int kAElems = BM * kStreamBK;  // one LDS stage
-  static_assert((NB == 2 || NB == 4) && MBW >= 1 && MBW <= 8 && (PF == 8 || PF == 16), "tile shape");
+  static_assert((NB == 2 || NB == 4) && MBW >= 1 && MBW <= 8 && (PF == 4 || PF == 8 || PF == 16),
+                "tile shape");
 };
 
 // One 16-byte direct global->LDS load per lane from base + voff bytes; lane l's
@@ -134,22 +135,25 @@ __device__ __forceinline__ void stream_finish() {
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
 }
 
-// One MFMA step: the A fragments of the MBW token blocks from the LDS stage,
-// then NB MFMAs per block.
-template <int MBW, int NB>
-__device__ __forceinline__ void stream_step(const bf16_t* As, int ch, const u32x4 (&bw)[NB],
-                                            f32x16 (&acc)[MBW][NB]) {
-  const int lane = threadIdx.x & 63;
-  // pipe_swz(32 m + r, ch) = 2048 m + r * 64 + ((ch ^ swz_key(r) ^ 4 (m & 1)) << 3)
-  // for r < 32: two lane offsets serve every block (the rest is an immediate)
-  const int r = lane & 31;
+// A fragments of the MBW token blocks for 16-wide step `ch / 2` of an LDS
+// stage.  pipe_swz(32 m + r, ch) = 2048 m + r * 64 + ((ch ^ swz_key(r) ^
+// 4 (m & 1)) << 3) for r < 32: two lane offsets serve every block (the rest is
+// an immediate).
+template <int MBW>
+__device__ __forceinline__ void stream_read_a(const bf16_t* As, int ch, bf16x8 (&fa)[MBW]) {
+  const int r = threadIdx.x & 31;
   const int off0 = r * kStreamBK + ((ch ^ swz_key(r)) << 3);
   const int off1 = r * kStreamBK + ((ch ^ swz_key(r) ^ 4) << 3);
-  bf16x8 fa[MBW];
 #pragma unroll
   for (int m = 0; m < MBW; ++m)
     fa[m] = __builtin_bit_cast(
         bf16x8, *reinterpret_cast<const u32x4*>(&As[2048 * m + ((m & 1) ? off1 : off0)]));
+}
+
+// One MFMA step: NB MFMAs per token block.
+template <int MBW, int NB>
+__device__ __forceinline__ void stream_mfma(const bf16x8 (&fa)[MBW], const u32x4 (&bw)[NB],
+                                            f32x16 (&acc)[MBW][NB]) {
 #pragma unroll
   for (int m = 0; m < MBW; ++m)
 #pragma unroll
@@ -179,7 +183,7 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
   constexpr int NS = kStreamNS;
   constexpr int MBW = BM / 32;
   constexpr int U = PF / 4;                          // blocks per unrolled body
-  static_assert(NS == 4 && (PF == 16 || PF == 8), "the schedule below is written for 4 stages");
+  static_assert(NS == 4 && (PF == 16 || PF == 8 || PF == 4), "the schedule below is written for 4 stages");
   // loads a wave issues per K block: MBW LDS loads and 4 NB weight loads.  The
   // stage of block kb was issued 3 blocks earlier; after it came 3 x 4 NB
   // weight loads and the MBW LDS loads of 2 later stages.
@@ -228,8 +232,9 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int slot = (4 * u + i) % PF;             // == (4 kb + i) mod PF
-      const int ch = 2 * i + (lane >> 5);
-      stream_step<MBW, NB>(As, ch, ss.bq[slot], acc);
+      bf16x8 fa[MBW];
+      stream_read_a<MBW>(As, 2 * i + (lane >> 5), fa);
+      stream_mfma<MBW, NB>(fa, ss.bq[slot], acc);
       // the step PF ahead: this tile's, or in the last blocks past its end the
       // next tile's (every tile has at least 16 steps)
       const bool from_next = last && (4 * u + i + PF >= 16);
@@ -254,7 +259,7 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
   int kb = 0;
   for (; kb < NKB - 4; kb += U) {                    // NKB is a multiple of 4
     kblock(kb, I0{}, No{});
-    kblock(kb + 1, I1{}, No{});
+    if constexpr (U >= 2) kblock(kb + 1, I1{}, No{});
     if constexpr (U == 4) {
       kblock(kb + 2, I2{}, No{});
       kblock(kb + 3, I3{}, No{});
