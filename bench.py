@@ -49,8 +49,8 @@ WRITE_FACTOR = 1.0
 GEMM_SOURCES = ("grouped_gemm.hip", "mma_stream.h", "lds_dma.h", "moe_internal.h")
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
-    "xs2_bf16_t4096_d2048": (628393.3, 36864.5,
-                             "efbb935ffc682c843b7eb0ef9e0cf6f2cb5a9a8a25da0e1cc67fa7fcfc75cc8d"),
+    "xs2_bf16_t4096_d2048": (624776.1, 36864.9,
+                             "379b39fed10f70f14cdf7e5a4ea84622f0b3d42530099587f44e333b50f48542"),
 }
 
 
