@@ -64,7 +64,7 @@ struct TileOut {
 // 256 output columns), computed by the weight-streaming pipeline
 // (mma_stream.h).  Wave w holds the gate block and the up block of the same 32
 // columns, so SwiGLU is applied in registers; outputs go straight from
-// registers to memory, four adjacent bf16 values (8 bytes) per lane and store.
+// registers to memory, eight adjacent bf16 values (16 bytes) per lane and store.
 template <int MODE, int BM, int NB, int PF>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   using ST = StreamTile<BM, NB, PF>;
@@ -178,18 +178,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       src.a_base = g.a_routed + static_cast<size_t>(rb + m0) * K;
     }
     // gathered rows: the token ids of the wave's 8 MBW consecutive rows come
-    // in one window of scalar loads (no vector-memory wait, which would also
-    // wait for the weight stream in flight); rows past the expert's last read
-    // other experts' (valid) ids and are dropped.  A window that would run
-    // past the end of the array (only near the last rows) reads per lane.
+    // in one window of scalar loads only (a vector load here would make the
+    // compiler wait for the whole weight stream in flight); near the end of
+    // the array the window's loads are clamped one by one.  Rows past the
+    // tile's last take its last row's id, like the rows of the other modes,
+    // so that their results equal that row's.
     const int wstart = rb + m0 + 8 * MBW * wave;
-    const bool window = gathered && wstart + 8 * MBW <= g.S;
     int win[8 * MBW];
-    if (window) {
+    int last_tok = 0;
+    if (gathered) {
       const __attribute__((address_space(4))) int32_t* gt =
-          (const __attribute__((address_space(4))) int32_t*)(g.gather) + wstart;
+          (const __attribute__((address_space(4))) int32_t*)(g.gather);
+      last_tok = gt[rb + m0 + valid - 1];
+      if (wstart + 8 * MBW <= g.S) {
 #pragma unroll
-      for (int i = 0; i < 8 * MBW; ++i) win[i] = gt[i];
+        for (int i = 0; i < 8 * MBW; ++i) win[i] = gt[wstart + i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8 * MBW; ++i) win[i] = gt[min(wstart + i, g.S - 1)];
+      }
     }
 #pragma unroll
     for (int q = 0; q < MBW; ++q) {
@@ -197,14 +204,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       chunk_source(stream_a_slot<MBW>(q, wave, lane), row, col);
       uint32_t r;
       if (gathered) {
-        int tok;
-        if (window) {
-          tok = win[8 * q];
+        int tok = win[8 * q];
 #pragma unroll
-          for (int i = 1; i < 8; ++i) tok = (lane >> 3) == i ? win[8 * q + i] : tok;
-        } else {
-          tok = g.gather[rb + min(m0 + row, M - 1)];
-        }
+        for (int i = 1; i < 8; ++i) tok = (lane >> 3) == i ? win[8 * q + i] : tok;
+        tok = row < valid ? tok : last_tok;
         r = static_cast<uint32_t>(min(max(tok, 0), g.T - 1));
       } else {
         r = static_cast<uint32_t>(min(row, valid - 1));
@@ -234,52 +237,97 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   StreamSrc<BM, NB> cur, nxt;
   TileOut ocur, onxt;
   StreamState<NB, PF> ss;
+  // A tile's outputs are rounded and packed, 8 bf16 per lane and store.  With
+  // 2 weight blocks per wave they wait in registers and are stored during the
+  // next tile's last K blocks, a few per block among its loads: stored at the
+  // tile's end they would queue behind the next tile's whole prefetch and
+  // hold every wave up.  The 4-block shapes have no registers to spare and
+  // store at the tile's end (the next tile's first waits count those stores).
+  // Rows past the tile's last rewrite its last row, whose values they repeat
+  // bit for bit, so the number of stores is a constant.
+  constexpr int kJ = MODE == kGateUp ? NB / 2 : NB;   // output blocks of 32 columns per wave
+  constexpr int kStores = MBW * kJ * 2;
+  constexpr bool kDefer = NB == 2;
+  constexpr int kPer = (kStores + 3) / 4;             // stores per tail block
+  uint4 pend[kStores];
+  TileOut opend;
+  bool has_pend = false;
+  auto store_pend = [&](int s_idx) {
+    const int m = s_idx / (2 * kJ), j = (s_idx / 2) % kJ, p = s_idx % 2;
+    const int row = min(32 * m + (lane & 31), opend.valid - 1);
+    bf16_t* dst = opend.out + static_cast<size_t>(row) * opend.ld + 8 * (lane >> 5) + 32 * j + 16 * p;
+    *reinterpret_cast<uint4*>(dst) = pend[s_idx];
+  };
   decode(pos, cur, ocur);
   stream_start<BM, NB, PF>(cur, ss, lds);
   for (int ti = pos; ti < total; ti += G) {
     const TileOut o = ocur;
     f32x16 acc[MBW][NB];
-    stream_tile<BM, NB, PF>(cur, nxt, [&]() {
+    stream_tile<BM, NB, PF, kDefer ? 0 : kStores>(cur, nxt, [&]() {
       if (ti + G >= total) return false;
       decode(ti + G, nxt, onxt);
       return true;
-    }, ss, lds, acc);
-    // epilogue: registers to memory; no LDS (other waves may still read the
-    // tile's last stage until the next tile's first barrier)
+    }, [&](auto u_tag) {
+      constexpr int u = decltype(u_tag)::value;
+      if (kDefer && has_pend) {
+#pragma unroll
+        for (int s_idx = u * kPer; s_idx < (u + 1) * kPer && s_idx < kStores; ++s_idx) store_pend(s_idx);
+      }
+    }, ss, lds, acc, !kDefer && has_pend);
+    // epilogue: round and pack.  Lane l holds columns 8q + 4 (l / 32) + 0..3
+    // of its token for q = 0..3; one lane-pair swap (lanes l and l + 32) gives
+    // lane l columns 16p + 0..7 and lane l + 32 columns 16p + 8..15.
 #pragma unroll
     for (int m = 0; m < MBW; ++m) {
-      const int row = 32 * m + (lane & 31);                     // token row inside the tile
-      if (row < o.valid) {
-        bf16_t* orow = o.out + static_cast<size_t>(row) * o.ld + 4 * (lane >> 5);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {            // registers 4q..4q+3: 4 adjacent columns
-          if (MODE == kGateUp) {
+      for (int j = 0; j < kJ; ++j) {
 #pragma unroll
-            for (int j = 0; j < NB / 2; ++j) {
-              float h[4];
+        for (int p = 0; p < 2; ++p) {          // registers 8p..8p+7: quads q = 2p, 2p + 1
+          uint32_t v[2][2];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
+          for (int h = 0; h < 2; ++h) {
+            const int q = 2 * p + h;
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (MODE == kGateUp) {
                 const float gv = acc[m][j][4 * q + e], uv = acc[m][j + NB / 2][4 * q + e];
-                h[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+                y[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+              } else {
+                y[e] = acc[m][j][4 * q + e];
               }
-              *reinterpret_cast<uint2*>(orow + 32 * j + 8 * q) =
-                  make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
             }
-          } else {
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-              *reinterpret_cast<uint2*>(orow + 32 * j + 8 * q) =
-                  make_uint2(pack_bf16x2(acc[m][j][4 * q], acc[m][j][4 * q + 1]),
-                             pack_bf16x2(acc[m][j][4 * q + 2], acc[m][j][4 * q + 3]));
+            v[h][0] = pack_bf16x2(y[0], y[1]);
+            v[h][1] = pack_bf16x2(y[2], y[3]);
           }
-          // a few accumulators at a time: reading them all out at once would
-          // need as many VGPRs, on top of the weight ring in flight
-          __builtin_amdgcn_sched_barrier(0);
+          // lanes < 32 keep quad 2p and take the upper lanes' quad 2p; lanes
+          // >= 32 take the lower lanes' quad 2p + 1 and keep theirs
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(v[0][c], v[1][c], false, false);
+            v[0][c] = sw[0];
+            v[1][c] = sw[1];
+          }
+          pend[(m * kJ + j) * 2 + p] = make_uint4(v[0][0], v[0][1], v[1][0], v[1][1]);
+          if (!kDefer) {
+            opend = o;
+            store_pend((m * kJ + j) * 2 + p);
+            // a few accumulators at a time: reading them all out at once
+            // would need as many VGPRs, on top of the weight ring in flight
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     }
+    opend = o;
+    has_pend = true;
     cur = nxt;
     ocur = onxt;
+  }
+  // the last tile's outputs
+  if (kDefer) {
+#pragma unroll
+    for (int s_idx = 0; s_idx < kStores; ++s_idx) store_pend(s_idx);
   }
   stream_finish();
 }

@@ -176,10 +176,18 @@ __device__ __forceinline__ void stream_mfma(const bf16x8 (&fa)[MBW], const u32x4
 // next() is called once, before the tile's last 4 blocks (so that the next
 // tile's sources are live only while they are needed); it fills nxt and
 // returns whether there is a next tile.
-template <int BM, int NB, int PF, typename Next>
+//
+// stored: the caller issued exactly ST vector-memory stores per wave after the
+// previous tile's loop (its epilogue).  Those stores sit between the LDS
+// stages of blocks 0..2 (issued in the previous tile's last blocks) and their
+// waits, so these waits count them too; vector-memory operations of a wave
+// retire in issue order (loads and stores alike), so a wait that counts them
+// still guarantees its stage has landed and no longer drains the loads issued
+// after it.  A count past the counter's range falls back to the plain wait.
+template <int BM, int NB, int PF, int ST, typename Next, typename Hook>
 __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, StreamSrc<BM, NB>& nxt, Next&& next,
-                                            StreamState<NB, PF>& ss, const bf16_t* lds,
-                                            f32x16 (&acc)[BM / 32][NB]) {
+                                            Hook&& tail_hook, StreamState<NB, PF>& ss, const bf16_t* lds,
+                                            f32x16 (&acc)[BM / 32][NB], bool stored) {
   constexpr int NS = kStreamNS;
   constexpr int MBW = BM / 32;
   constexpr int U = PF / 4;                          // blocks per unrolled body
@@ -190,6 +198,7 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
   constexpr int kW = 4 * NB * (NS - 1);
   constexpr int kKeep = kW + 2 * MBW;
   static_assert(kKeep < 64, "vmcnt range");
+  constexpr int kStoreComp = kKeep + ST <= 63 ? ST : 0;   // added to the waits of blocks 0..2
   const int lane = threadIdx.x & 63;
   const int NKB = cur.nkb;
 #pragma unroll
@@ -208,14 +217,26 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
     constexpr bool last = decltype(last_tag)::value; // u-th of the tile's last 4 blocks
     // wait for this block's stage; in the last blocks the later stages may be
     // the next tile's, or none after the last tile
+    const bool comp = kStoreComp > 0 && stored && kb < NS - 1;
     if constexpr (last && u == 3) {
-      if (has_next) __builtin_amdgcn_s_waitcnt(vmcnt_only(kKeep));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_only(kW));
+      if (has_next) {
+        if (comp) __builtin_amdgcn_s_waitcnt(vmcnt_only(kKeep + kStoreComp));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_only(kKeep));
+      } else {
+        if (comp) __builtin_amdgcn_s_waitcnt(vmcnt_only(kW + kStoreComp));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_only(kW));
+      }
     } else if constexpr (last && u == 2) {
-      if (has_next) __builtin_amdgcn_s_waitcnt(vmcnt_only(kKeep));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_only(kW + MBW));
+      if (has_next) {
+        if (comp) __builtin_amdgcn_s_waitcnt(vmcnt_only(kKeep + kStoreComp));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_only(kKeep));
+      } else {
+        if (comp) __builtin_amdgcn_s_waitcnt(vmcnt_only(kW + MBW + kStoreComp));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_only(kW + MBW));
+      }
     } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(kKeep));
+      if (comp) __builtin_amdgcn_s_waitcnt(vmcnt_only(kKeep + kStoreComp));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_only(kKeep));
     }
     __builtin_amdgcn_s_barrier();
     // refill the stage read in the previous block with block kb + 3
@@ -228,6 +249,7 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
         if (has_next) stream_issue(nxt, u - 1, dst);
       }
     }
+    if constexpr (last) tail_hook(u_tag);
     const bf16_t* As = lds + ss.st * (BM * kStreamBK);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -19,16 +19,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
-}
+// fp32 -> bf16 by gfx950's v_cvt_pk_bf16_f32: round to nearest, ties to
+// even (the default rounding mode); NaN stays NaN, overflow goes to inf.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return static_cast<bf16_t>(pack_bf16x2(f, 0.0f));
 }
 
 __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-a)); }
