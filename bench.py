@@ -11,7 +11,8 @@ tokens/s of the layer, plus
   roofline      the dominant kernel (the gate/up grouped GEMM with its SwiGLU
                 epilogue): algorithmic bytes (or FLOPs) per launch divided by its
                 average duration, measured with HIP events recorded on the stream
-                it runs on, against the MI355X peak that bounds it;
+                it runs on around its launches in every fourth timed step,
+                against the MI355X peak that bounds it;
   cpu_baseline  the CPU oracle (fp64 NumPy, self-contained routing) timed on the
                 host cores on the same workload.
 
@@ -34,6 +35,7 @@ if ROOT not in sys.path:
 from mixture_experts_transformer_moe_amd import configs  # noqa: E402
 
 METRIC = "MoE-layer tokens/s at 1 MI355X; % of bf16 MFMA peak (prefill) / HBM GB/s (decode)"
+EV_EVERY = 4
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
@@ -49,8 +51,8 @@ WRITE_FACTOR = 1.0
 GEMM_SOURCES = ("grouped_gemm.hip", "mma_stream.h", "lds_dma.h", "moe_internal.h")
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
-    "xs2_bf16_t4096_d2048": (624776.1, 36864.9,
-                             "379b39fed10f70f14cdf7e5a4ea84622f0b3d42530099587f44e333b50f48542"),
+    "xs2_bf16_t4096_d2048": (622545.5, 36967.6,
+                             "51260bcd3f4078d32d968f75837fb64197a542c99b7a239f1c60064e45e14d88"),
 }
 
 
@@ -130,8 +132,9 @@ def cpu_oracle_baseline(s, inp_host, target_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    # the clocks take some tens of milliseconds of load to settle
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=configs.BENCH_WORKLOAD, choices=sorted(configs.WORKLOADS))
     ap.add_argument("--x-perm", action="store_true",
                     help="materialise x_perm in moe_permute and read it in the first GEMM "
@@ -182,15 +185,18 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # the gate/up launch of every EV_EVERY-th timed step is bracketed by two
+    # events on its stream (each event costs the stream a few microseconds)
+    timed = list(range(0, args.steps, EV_EVERY))
+    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for i in timed}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    gate_up_ms = float(np.mean([a.elapsed_time(z) for a, z in evs]))
+    gate_up_ms = float(np.mean([a.elapsed_time(z) for a, z in evs.values()]))
 
     if args.copy_mib > 0:
         n = args.copy_mib << 20
