@@ -18,7 +18,7 @@
 //     the workgroups that share a weight tile run at the same time behind the
 //     same L2, and every workgroup gets the same number of tiles to within
 //     one; the shared expert's row-block height is picked so that its tiles
-//     fill the last round;
+//     fill the last round (gate_up spreads them through all rounds instead);
 //   * BM x 256 tiles (BM by the mean rows per expert, so an expert's rows
 //     mostly fit one tile and its weights stream once), one workgroup per CU;
 //     weights, packed in MFMA fragment order, stream from HBM straight into
@@ -146,6 +146,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     // out of the tile loop it would hold registers across the whole stream
     int lane = tid & 63;
     asm volatile("" : "+v"(lane));
+    if (MODE == kGateUp) {
+      // gate_up: the shared expert's tiles (weights L2-resident after the
+      // first few) are spread evenly through the schedule instead of filling
+      // the last round, so that every round keeps most CUs on the HBM weight
+      // stream: schedule slot ti holds shared tile c0 when floor((ti + 1) ns /
+      // total) steps past c0 = floor(ti ns / total), else routed tile ti - c1
+      const int routed_total = __builtin_amdgcn_readfirstlane(tile_end[E - 1]);
+      const int ns = total - routed_total;
+      const int c1 = static_cast<int>((static_cast<long long>(ti) + 1) * ns / total);
+      const int c0 = static_cast<int>(static_cast<long long>(ti) * ns / total);
+      ti = c1 > c0 ? routed_total + c0 : ti - c1;
+    }
     int lo = 0, hi = E;                     // group: first with tile_end > ti
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
