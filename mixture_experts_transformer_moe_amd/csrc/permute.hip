@@ -2,16 +2,16 @@
 // fuse into their grouped GEMM ("copy expert tokens in expert order", "Laguna
 // M.1/XS.2 Technical Report", Key claims, report section 3.1.2, Fig. 2).
 //
-// Three index kernels and one copy, all deterministic (integer work only; LDS
+// Two index kernels and one copy, all deterministic (integer work only; LDS
 // atomics count and set bits, which gives the same result in any order):
 //   hist    one block per 256 tokens: per-block expert histogram -> workspace
-//   scan    one block: per-expert totals (counts), exclusive scan over experts
-//           (offsets), and for every block the first position of each expert's
-//           tokens in that block (written back over the histogram)
-//   scatter one block per 256 tokens: the rank of token t among the block's
-//           tokens of expert e is a popcount over an LDS bitmap of which tokens
-//           chose e; position = block base + rank, so each expert's tokens end
-//           up in ascending token order
+//   scatter one block per 256 tokens: from all the blocks' histograms, each
+//           block derives the per-expert totals, their exclusive scan over the
+//           experts and its own first position of each expert's tokens (block
+//           0 also writes counts and offsets); the rank of token t among the
+//           block's tokens of expert e is a popcount over an LDS bitmap of
+//           which tokens chose e; position = block base + rank, so each
+//           expert's tokens end up in ascending token order
 //   gather  x_perm[p] = x[sorted_token[p]] with 16-byte loads and stores,
 //           flattened over all (row, chunk) pairs
 #include "moe_internal.h"
@@ -21,6 +21,7 @@ namespace {
 
 constexpr int kTB = 256;        // tokens per block
 constexpr int kMaxE = 256;
+static_assert(kTB == kMaxE, "the scatter kernel keeps one thread per expert");
 
 __device__ __forceinline__ int clamp_e(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
@@ -36,60 +37,58 @@ __global__ __launch_bounds__(kTB) void perm_hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += kTB) blk[static_cast<size_t>(blockIdx.x) * E + e] = hist[e];
 }
 
-// 1024 threads: thread (part, e) sums a quarter of the blocks of expert e.
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ blk, int nb, int E,
-                                                         int S, int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ offsets) {
-  __shared__ int32_t part_sum[4][kMaxE];
-  __shared__ int32_t scan[kMaxE];
-  const int e = threadIdx.x & (kMaxE - 1);
-  const int part = threadIdx.x >> 8;
-  const int chunk = (nb + 3) / 4;
-  const int b_lo = part * chunk;
-  const int b_hi = min(nb, b_lo + chunk);
-  int sum = 0;
-  if (e < E)
-    for (int b = b_lo; b < b_hi; ++b) sum += blk[static_cast<size_t>(b) * E + e];
-  part_sum[part][e] = sum;
-  __syncthreads();
-  if (part == 0) {
-    const int c = e < E ? part_sum[0][e] + part_sum[1][e] + part_sum[2][e] + part_sum[3][e] : 0;
-    scan[e] = c;
-    if (e < E) counts[e] = c;
-  }
-  __syncthreads();
-  // inclusive Hillis-Steele scan over the 256 expert totals
-  for (int off = 1; off < kMaxE; off <<= 1) {
-    int v = 0;
-    if (part == 0 && e >= off) v = scan[e - off];
-    __syncthreads();
-    if (part == 0) scan[e] += v;
-    __syncthreads();
-  }
-  const int excl_e = e == 0 ? 0 : scan[e - 1];
-  if (part == 0 && e < E) offsets[e] = excl_e;
-  if (threadIdx.x == 0) offsets[E] = S;
-  if (e < E) {
-    int base = excl_e;
-    for (int p = 0; p < part; ++p) base += part_sum[p][e];
-    for (int b = b_lo; b < b_hi; ++b) {
-      const size_t i = static_cast<size_t>(b) * E + e;
-      const int c = blk[i];
-      blk[i] = base;
-      base += c;
-    }
-  }
-}
-
+// Thread e of every block: expert e's total over all nb blocks and its count
+// in the blocks before this one, then an exclusive scan of the totals over
+// the experts in LDS.
 __global__ __launch_bounds__(kTB) void perm_scatter_kernel(const int32_t* __restrict__ idx, int T,
-                                                           int E, int k,
+                                                           int E, int k, int nb, int S,
                                                            const int32_t* __restrict__ blk,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ sorted_token,
                                                            int32_t* __restrict__ slot_of) {
   __shared__ uint32_t chose[kMaxE][kTB / 32];   // bit (t mod 256) of row e: token chose e
   __shared__ int32_t base[kMaxE];
+  __shared__ int32_t scan[kMaxE];
+  const int e = threadIdx.x;                      // kTB == kMaxE: one thread per expert
   for (int i = threadIdx.x; i < kMaxE * (kTB / 32); i += kTB) (&chose[0][0])[i] = 0u;
-  for (int e = threadIdx.x; e < E; e += kTB) base[e] = blk[static_cast<size_t>(blockIdx.x) * E + e];
+  int total = 0, before = 0;
+  if (e < E) {
+    int b = 0;
+    for (; b + 8 <= nb; b += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = blk[static_cast<size_t>(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        total += c[u];
+        before += b + u < static_cast<int>(blockIdx.x) ? c[u] : 0;
+      }
+    }
+    for (; b < nb; ++b) {
+      const int c = blk[static_cast<size_t>(b) * E + e];
+      total += c;
+      before += b < static_cast<int>(blockIdx.x) ? c : 0;
+    }
+  }
+  scan[e] = total;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the expert totals
+  for (int off = 1; off < kMaxE; off <<= 1) {
+    const int v = e >= off ? scan[e - off] : 0;
+    __syncthreads();
+    scan[e] += v;
+    __syncthreads();
+  }
+  const int excl = scan[e] - total;
+  base[e] = excl + before;
+  if (blockIdx.x == 0) {
+    if (e < E) {
+      counts[e] = total;
+      offsets[e] = excl;
+    }
+    if (e == 0) offsets[E] = S;
+  }
   __syncthreads();
   const int local = threadIdx.x;
   const int t = blockIdx.x * kTB + local;
@@ -101,10 +100,10 @@ __global__ __launch_bounds__(kTB) void perm_scatter_kernel(const int32_t* __rest
   __syncthreads();
   if (t < T) {
     for (int j = 0; j < k; ++j) {
-      const int e = clamp_e(idx[static_cast<size_t>(t) * k + j], E);
-      int rank = __popc(chose[e][word] & (bit - 1u));
-      for (int w = 0; w < word; ++w) rank += __popc(chose[e][w]);
-      const int pos = base[e] + rank;
+      const int ej = clamp_e(idx[static_cast<size_t>(t) * k + j], E);
+      int rank = __popc(chose[ej][word] & (bit - 1u));
+      for (int w = 0; w < word; ++w) rank += __popc(chose[ej][w]);
+      const int pos = base[ej] + rank;
       slot_of[static_cast<size_t>(t) * k + j] = pos;
       sorted_token[pos] = t;
     }
@@ -156,9 +155,8 @@ hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x,
   hipError_t err;
   perm_hist_kernel<<<nb, kTB, 0, st>>>(idx, s.T, s.E, s.k, blk);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  perm_scan_kernel<<<1, 1024, 0, st>>>(blk, nb, s.E, S, counts, offsets);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  perm_scatter_kernel<<<nb, kTB, 0, st>>>(idx, s.T, s.E, s.k, blk, sorted_token, slot_of);
+  perm_scatter_kernel<<<nb, kTB, 0, st>>>(idx, s.T, s.E, s.k, nb, S, blk, counts, offsets,
+                                          sorted_token, slot_of);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (x_perm) {
     const int elem = s.dtype == MOE_BF16 ? 2 : 4;
