@@ -68,9 +68,15 @@ PREFILL_OUTLIER_T32768 = MoEShape("prefill_outlier_bf16_t32768_d2048", T=32768, 
                                   k=8, F=512, Fs=512, alpha=2.5, dtype="bf16", seed=4,
                                   outlier_frac=0.1)
 
+# M.1's own routing at its widths: top-16 of 256 with routed scale 1
+# ("Laguna-M.1-base", Mixture of experts: experts per token, routed scaling
+# factor).
+M1_TOP16_T8192 = MoEShape("m1_top16_bf16_t8192_d4096", T=8192, D=4096, E=256, k=16, F=1024,
+                          Fs=1024, alpha=1.0, dtype="bf16", seed=5)
+
 WORKLOADS: Dict[str, MoEShape] = {s.name: s for s in
                                   (TINY_F32, XS2_T4096, M1_T8192, DECODE_SKEW_T32,
-                                   PREFILL_OUTLIER_T32768)}
+                                   PREFILL_OUTLIER_T32768, M1_TOP16_T8192)}
 
 # The single-GPU benchmark workload: the XS.2-shaped layer.
 BENCH_WORKLOAD = XS2_T4096.name

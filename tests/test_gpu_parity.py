@@ -84,7 +84,8 @@ def test_small_bf16_gather_mode_matches_x_perm_mode():
 
 @pytest.mark.parametrize("name", [configs.XS2_T4096.name, configs.M1_T8192.name,
                                   configs.DECODE_SKEW_T32.name,
-                                  configs.PREFILL_OUTLIER_T32768.name])
+                                  configs.PREFILL_OUTLIER_T32768.name,
+                                  configs.M1_TOP16_T8192.name])
 def test_full_size_workload_sampled_parity(name):
     sampled_parity(configs.get(name))
 
@@ -100,6 +101,7 @@ def test_decode_workload_full_parity():
 EDGE = {
     "k1": dict(k=1),
     "k_eq_E": dict(E=16, k=16),
+    "k16_alpha1_E64": dict(E=64, k=16, alpha=1.0),
     "E1_k1": dict(E=1, k=1),
     "no_shared": dict(Fs=0),
     "T1": dict(T=1),

@@ -300,10 +300,17 @@ def test_invariants_hold_on_small_workload_and_catch_corruption():
 def test_workload_constants_match_pages():
     f = _facts()
     for s in configs.WORKLOADS.values():
-        if s.dtype == "bf16":
+        if s is configs.M1_TOP16_T8192:                         # M.1's own routing
             assert s.E == f["routed_experts"]["value"]
-            assert s.k == f["xs2_top_k"]["value"]
-        assert s.alpha == f["xs2_routed_scale"]["value"]
+            assert s.k == f["m1_top_k"]["value"]
+            assert s.alpha == f["m1_routed_scale"]["value"]
+            assert s.D == f["m1_d_model"]["value"]
+            assert s.F == f["m1_expert_dim"]["value"]
+        else:
+            if s.dtype == "bf16":
+                assert s.E == f["routed_experts"]["value"]
+                assert s.k == f["xs2_top_k"]["value"]
+            assert s.alpha == f["xs2_routed_scale"]["value"]
         assert s.Fs == s.F                                      # one shared expert per layer
     assert configs.M1_T8192.D == f["m1_d_model"]["value"]
     assert configs.M1_T8192.F == f["m1_expert_dim"]["value"]
