@@ -72,24 +72,31 @@ def measured_traffic(workload: str):
     return (rec[0] * FETCH_FACTOR + rec[1] * WRITE_FACTOR) * 1024.0
 
 
-def gate_up_work(s: configs.MoEShape, n_touched: int):
+def gate_up_work(s: configs.MoEShape, n_touched: int, fp8: bool = False):
     """Algorithmic FLOPs and HBM bytes of one gate/up grouped-GEMM launch.
 
     bytes = weights of the touched routed experts (2F x D each) + shared weights
+            (1 byte per weight and a 4-byte scale per row with FP8 weights)
           + A rows read (k*T routed rows and T shared rows of width D)
           + h written ((k*T*F + T*Fs) elements).
     """
     el = 2 if s.dtype == "bf16" else 4
     flops = 4.0 * s.S * s.D * s.F + 4.0 * s.T * s.D * s.Fs
-    w = (n_touched * 2 * s.F * s.D + 2 * s.Fs * s.D) * el
+    if fp8:
+        w = (n_touched * 2 * s.F + 2 * s.Fs) * (s.D + 4)
+    else:
+        w = (n_touched * 2 * s.F * s.D + 2 * s.Fs * s.D) * el
     a = (s.S + (s.T if s.Fs else 0)) * s.D * el
     h = (s.S * s.F + s.T * s.Fs) * el
     return flops, float(w + a + h)
 
 
-def cpu_oracle_baseline(s, inp_host, target_s: float = 12.0):
-    """Times the CPU oracle (self-contained fp64 forward) on host cores."""
+def cpu_oracle_baseline(s, inp_host, target_s: float = 12.0, fp8: bool = False):
+    """Times the CPU oracle (self-contained fp64 forward) on host cores (with FP8
+    weights: the oracle's FP8 reading of every expert, quantised as it goes)."""
     from oracle import moe_oracle as O
+    from oracle import fp8_oracle as F8
+    wrap = F8.Fp8Weights if fp8 else (lambda inputs: inputs)
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -111,19 +118,19 @@ def cpu_oracle_baseline(s, inp_host, target_s: float = 12.0):
     # probe on a small slice, then size the sample to about target_s seconds
     n0 = min(s.T, 256)
     t0 = time.perf_counter()
-    O.forward(Sub(n0), s.alpha, s.k)
+    O.forward(wrap(Sub(n0)), s.alpha, s.k)
     probe = time.perf_counter() - t0
     n = s.T if probe * s.T / n0 <= target_s * 1.5 else max(n0, int(n0 * target_s / probe))
     n = min(n, s.T)
     passes, tokens, t0 = 0, 0, time.perf_counter()
     while True:
-        O.forward(Sub(n), s.alpha, s.k)
+        O.forward(wrap(Sub(n)), s.alpha, s.k)
         passes += 1
         tokens += n
         el = time.perf_counter() - t0
         if el >= min(target_s, 10.0) or passes >= 8:
             break
-    sample = (f"self-contained fp64 oracle forward over the first {n} of {s.T} tokens "
+    sample = (f"self-contained fp64 oracle forward{' with FP8 weights' if fp8 else ''} over the first {n} of {s.T} tokens "
               f"(all experts they select), {passes} pass(es), weights already in host memory")
     return {"value": tokens / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": sample, "seconds": round(el, 3)}
@@ -139,6 +146,9 @@ def main():
     ap.add_argument("--x-perm", action="store_true",
                     help="materialise x_perm in moe_permute and read it in the first GEMM "
                          "(default: the first GEMM gathers token rows through sorted_token)")
+    ap.add_argument("--fp8-weights", action="store_true",
+                    help="expert weights in FP8 (E4M3, per-row scales; moe_quantize_weights_fp8) "
+                         "and the FP8 grouped GEMMs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB device to device "
@@ -161,7 +171,8 @@ def main():
     host = {"x": inp.x, "w_router": inp.w_router, "bias": inp.bias, "wgu": wgu, "wd": wd,
             "shared": inp.shared()}
     # expert weights are packed once into MFMA fragment order (moe_pack_weights)
-    w = binding.upload_weights(s, inp.w_router, inp.bias, wgu, wd, host["shared"], dev)
+    w = binding.upload_weights(s, inp.w_router, inp.bias, wgu, wd, host["shared"], dev,
+                               fp8=args.fp8_weights)
     x = binding.to_device(inp.x, s, dev)
     b = binding.alloc_buffers(s, dev, with_x_perm=args.x_perm)
     c = binding.make_shape(s)
@@ -173,12 +184,21 @@ def main():
                             b.x_perm, b.workspace, stream)
         if ev is not None:
             ev[0].record(stream)
-        binding.moe_grouped_gate_up(c, b.x_perm, b.sorted_token, x, b.offsets, w.w_gate_up,
-                                    w.ws_gate_up, b.h, stream)
+        if w.fp8:
+            binding.moe_grouped_gate_up_fp8(c, b.x_perm, b.sorted_token, x, b.offsets, w.w_gate_up,
+                                            w.w_gate_up_scale, w.ws_gate_up, w.ws_gate_up_scale,
+                                            b.h, stream)
+        else:
+            binding.moe_grouped_gate_up(c, b.x_perm, b.sorted_token, x, b.offsets, w.w_gate_up,
+                                        w.ws_gate_up, b.h, stream)
         if ev is not None:
             ev[1].record(stream)
-        binding.moe_grouped_down(c, b.h, b.offsets, w.w_down, w.ws_down, b.y_perm, b.y_shared,
-                                 stream)
+        if w.fp8:
+            binding.moe_grouped_down_fp8(c, b.h, b.offsets, w.w_down, w.w_down_scale, w.ws_down,
+                                         w.ws_down_scale, b.y_perm, b.y_shared, stream)
+        else:
+            binding.moe_grouped_down(c, b.h, b.offsets, w.w_down, w.ws_down, b.y_perm, b.y_shared,
+                                     stream)
         binding.moe_combine(c, b.y_perm, b.y_shared, b.slot_of, b.topk_w, b.out, stream)
 
     for _ in range(args.warmup):
@@ -209,7 +229,7 @@ def main():
 
     counts = b.counts.cpu().numpy()
     n_touched = int(np.count_nonzero(counts))
-    flops, nbytes = gate_up_work(s, n_touched)
+    flops, nbytes = gate_up_work(s, n_touched, args.fp8_weights)
     intensity = flops / nbytes
     peak_flops = PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_F32_TFLOPS
     ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -221,7 +241,10 @@ def main():
         achieved = flops / (gate_up_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_flops,
                 "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4)}
-    roof.update({"traffic": measured_traffic(s.name), "kernel": "grouped_gemm_kernel<gate_up> (moe_grouped_gate_up)",
+    traffic = None if args.fp8_weights else measured_traffic(s.name)
+    kname = ("grouped_gemm_kernel<gate_up, FP8 weights> (moe_grouped_gate_up_fp8)" if args.fp8_weights
+             else "grouped_gemm_kernel<gate_up> (moe_grouped_gate_up)")
+    roof.update({"traffic": traffic, "kernel": kname,
                  "kernel_ms": round(gate_up_ms, 4), "algorithmic_bytes": nbytes,
                  "algorithmic_flops": flops,
                  "mfma_tflops": round(flops / (gate_up_ms * 1e-3) / 1e12, 1)})
@@ -231,7 +254,7 @@ def main():
     layer_tflops = s.flops() / (ms * 1e-3) / 1e12
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_oracle_baseline(s, host)
+        cpu = cpu_oracle_baseline(s, host, fp8=args.fp8_weights)
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -239,7 +262,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": s.name, "tokens": s.T, "d_model": s.D, "experts": s.E,
                    "top_k": s.k, "expert_width": s.F, "shared_width": s.Fs, "alpha": s.alpha,
-                   "a_rows": "x_perm" if args.x_perm else "gather", "parallelism": "single-gpu"},
+                   "a_rows": "x_perm" if args.x_perm else "gather",
+                   "expert_weights": "fp8-e4m3-row-scaled" if args.fp8_weights else "bf16",
+                   "parallelism": "single-gpu"},
         "layer_tflops": round(layer_tflops, 1),
         "experts_touched": n_touched, "rows_per_expert_max": int(counts.max()),
         "roofline": roof, "cpu_baseline": cpu,

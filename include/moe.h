@@ -179,6 +179,60 @@ int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* s
                     const void* w_down, const void* ws_gate_up, const void* ws_down, void* h,
                     void* y_perm, void* y_shared, void* stream);
 
+/* ---- FP8 expert weights --------------------------------------------------
+ * The XS.2 release ships FP8 recipes for its MoE layers ("Laguna M.1/XS.2
+ * Technical Report", Key claims: FP8, INT4 and NVFP4 quantisation of the MoE
+ * layers) without encoding details; this library's reading:
+ *   - element format OCP FP8 E4M3 (bias 7, largest finite 448, subnormals,
+ *     no infinities; gfx950's native FP8);
+ *   - one fp32 scale per output row of every weight matrix:
+ *     s_r = max_c |w[r,c]| / 448 in fp32 (1 for an all-zero row);
+ *   - code[r,c] = E4M3 nearest to w[r,c] / s_r (fp32 quotient), ties to the
+ *     even code, magnitudes past 448 saturating to 448;
+ *   - the layer runs with the weights code * s_r.  The GEMMs widen the codes
+ *     to bf16 (exact), multiply by the bf16 activations with fp32
+ *     accumulation, and apply s_r to the accumulated row before the SwiGLU /
+ *     the rounding, which equals the product with code * s_r in exact
+ *     arithmetic.
+ * Activations stay bf16 (shape dtype MOE_BF16; anything else returns
+ * MOE_ERR_UNSUPPORTED).  Weights must be finite (non-finite inputs give
+ * unspecified codes). */
+
+/* Bytes of `count` FP8 [rows, cols] matrices (count * rows * cols); 0 unless
+ * rows and cols are multiples of 32. */
+size_t moe_fp8_packed_bytes(int64_t count, int32_t rows, int32_t cols);
+
+/* Quantise bf16 weights to FP8 and pack them for moe_grouped_gate_up_fp8 /
+ * moe_grouped_down_fp8 (a one-time pass when weights are loaded).
+ *   w       [count, rows, cols] bf16, row-major, rows = output rows (e.g.
+ *           w_gate_up as [E, 2F, D], w_down as [E, D, F])
+ *   w_fp8   moe_fp8_packed_bytes(count, rows, cols) bytes, out
+ *   scales  [count, rows] fp32, out: s_r per matrix row
+ *   rows % 32 == 0, cols % 32 == 0 (else MOE_ERR_INVALID_ARG); the three buffers
+ *   must not overlap.
+ * Layout: matrix i starts at byte i * rows * cols; in it, the code of (r, c)
+ * sits at byte
+ *   ((r / 32) * (cols / 32) + c / 32) * 1024 + ((r % 32) + 32 * ((c % 16) / 8)) * 16
+ *     + ((c % 32) / 16) * 8 + c % 8,
+ * i.e. 32 x 32 blocks of 1 KB in which lane l's 16 bytes are its 8 codes of two
+ * consecutive 16-wide K steps of a 32x32x16 MFMA operand. */
+int moe_quantize_weights_fp8(const void* w, void* w_fp8, float* scales, int64_t count, int32_t rows,
+                             int32_t cols, void* stream);
+
+/* moe_grouped_gate_up with FP8 weights: the same computation and buffers, with
+ * w_gate_up / ws_gate_up replaced by moe_quantize_weights_fp8's codes and
+ * scales (w_gate_up_scale [E, 2F], ws_gate_up_scale [2Fs]; the shared pair is
+ * ignored, may be NULL, when Fs == 0). */
+int moe_grouped_gate_up_fp8(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
+                            const void* x, const int32_t* offsets, const void* w_gate_up,
+                            const float* w_gate_up_scale, const void* ws_gate_up,
+                            const float* ws_gate_up_scale, void* h, void* stream);
+
+/* moe_grouped_down with FP8 weights (w_down_scale [E, D], ws_down_scale [D]). */
+int moe_grouped_down_fp8(const moe_shape* shape, const void* h, const int32_t* offsets,
+                         const void* w_down, const float* w_down_scale, const void* ws_down,
+                         const float* ws_down_scale, void* y_perm, void* y_shared, void* stream);
+
 /* Combine: out[t] = y_shared[t] + sum_{j=0..k-1} (alpha * topk_w[t,j]) * y_perm[slot_of[t,j]],
  * accumulated in fp32 in slot order and rounded once to elem ("Laguna M.1/XS.2
  * Technical Report", Key claims: routed output modulated by alpha before

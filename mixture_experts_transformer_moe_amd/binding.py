@@ -26,7 +26,8 @@ MOE_F32, MOE_BF16 = 0, 1
 # the entry points include/moe.h declares
 EXPORTS = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
            "moe_route", "moe_permute", "moe_pack_weights", "moe_packed_bytes", "moe_grouped_gate_up",
-           "moe_grouped_down", "moe_grouped_ffn", "moe_combine")
+           "moe_grouped_down", "moe_grouped_ffn", "moe_fp8_packed_bytes", "moe_quantize_weights_fp8",
+           "moe_grouped_gate_up_fp8", "moe_grouped_down_fp8", "moe_combine")
 
 
 class moe_shape(ctypes.Structure):
@@ -77,6 +78,15 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_down.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P]
         L.moe_grouped_ffn.restype = ctypes.c_int
         L.moe_grouped_ffn.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_fp8_packed_bytes.restype = ctypes.c_size_t
+        L.moe_fp8_packed_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+        L.moe_quantize_weights_fp8.restype = ctypes.c_int
+        L.moe_quantize_weights_fp8.argtypes = [_P, _P, _P, ctypes.c_int64, ctypes.c_int32,
+                                               ctypes.c_int32, _P]
+        L.moe_grouped_gate_up_fp8.restype = ctypes.c_int
+        L.moe_grouped_gate_up_fp8.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_grouped_down_fp8.restype = ctypes.c_int
+        L.moe_grouped_down_fp8.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine.argtypes = [_SP, _P, _P, _P, _P, _P, _P]
         _lib = L
@@ -173,6 +183,48 @@ def moe_grouped_ffn(shape, x_perm, sorted_token, x, offsets, w_gate_up, w_down, 
                                  _stream(stream)), "moe_grouped_ffn")
 
 
+def moe_fp8_packed_bytes(count, rows, cols) -> int:
+    return int(lib().moe_fp8_packed_bytes(int(count), int(rows), int(cols)))
+
+
+def moe_quantize_weights_fp8(w, w_fp8, scales, count, rows, cols, stream=None):
+    _check(lib().moe_quantize_weights_fp8(_ptr(w), _ptr(w_fp8), _ptr(scales), int(count), int(rows),
+                                          int(cols), _stream(stream)), "moe_quantize_weights_fp8")
+
+
+def quantize_fp8(w: torch.Tensor, stream=None):
+    """FP8 codes (flat uint8, packed) and row scales (float32 [count, rows]) of a
+    bf16 [rows, cols] or [count, rows, cols] weight tensor."""
+    if w.dim() == 2:
+        count, rows, cols = 1, w.shape[0], w.shape[1]
+    else:
+        count, rows, cols = w.shape
+    nbytes = moe_fp8_packed_bytes(count, rows, cols)
+    if nbytes == 0 and count * rows * cols > 0:
+        raise MoEError(MOE_ERR_INVALID_ARG, f"moe_fp8_packed_bytes: cannot pack [{count}, {rows}, {cols}]")
+    codes = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    scales = torch.empty((count, rows), dtype=torch.float32, device=w.device)
+    moe_quantize_weights_fp8(w.contiguous(), codes, scales, count, rows, cols, stream)
+    return codes, scales
+
+
+def moe_grouped_gate_up_fp8(shape, x_perm, sorted_token, x, offsets, w_gate_up, w_gate_up_scale,
+                            ws_gate_up, ws_gate_up_scale, h, stream=None):
+    _check(lib().moe_grouped_gate_up_fp8(ctypes.byref(shape), _ptr(x_perm), _ptr(sorted_token),
+                                         _ptr(x), _ptr(offsets), _ptr(w_gate_up),
+                                         _ptr(w_gate_up_scale), _ptr(ws_gate_up),
+                                         _ptr(ws_gate_up_scale), _ptr(h), _stream(stream)),
+           "moe_grouped_gate_up_fp8")
+
+
+def moe_grouped_down_fp8(shape, h, offsets, w_down, w_down_scale, ws_down, ws_down_scale, y_perm,
+                         y_shared, stream=None):
+    _check(lib().moe_grouped_down_fp8(ctypes.byref(shape), _ptr(h), _ptr(offsets), _ptr(w_down),
+                                      _ptr(w_down_scale), _ptr(ws_down), _ptr(ws_down_scale),
+                                      _ptr(y_perm), _ptr(y_shared), _stream(stream)),
+           "moe_grouped_down_fp8")
+
+
 def moe_combine(shape, y_perm, y_shared, slot_of, topk_w, out, stream=None):
     _check(lib().moe_combine(ctypes.byref(shape), _ptr(y_perm), _ptr(y_shared), _ptr(slot_of),
                              _ptr(topk_w), _ptr(out), _stream(stream)), "moe_combine")
@@ -236,33 +288,52 @@ def alloc_buffers(s: MoEShape, device="cuda", with_x_perm: bool = True) -> Layer
 
 @dataclass
 class LayerWeights:
-    """Layer weights on the device; expert weights in the packed layout."""
+    """Layer weights on the device; expert weights in the packed layout (bf16),
+    or FP8 codes with their row scales (``fp8``)."""
     w_router: torch.Tensor
     bias: Optional[torch.Tensor]
     w_gate_up: torch.Tensor       # E packed [2F, D] matrices (flat)
     w_down: torch.Tensor          # E packed [D, F] matrices (flat)
     ws_gate_up: Optional[torch.Tensor]
     ws_down: Optional[torch.Tensor]
+    fp8: bool = False
+    w_gate_up_scale: Optional[torch.Tensor] = None    # FP8: [E, 2F]
+    w_down_scale: Optional[torch.Tensor] = None       # FP8: [E, D]
+    ws_gate_up_scale: Optional[torch.Tensor] = None   # FP8: [1, 2Fs]
+    ws_down_scale: Optional[torch.Tensor] = None      # FP8: [1, D]
 
 
-def upload_weights(s: MoEShape, w_router, bias, wgu, wd, shared, device="cuda") -> LayerWeights:
-    """Host arrays in storage encoding -> LayerWeights (expert weights packed on the device)."""
+def upload_weights(s: MoEShape, w_router, bias, wgu, wd, shared, device="cuda",
+                   fp8: bool = False) -> LayerWeights:
+    """Host arrays in storage encoding -> LayerWeights (expert weights packed on
+    the device, or quantised to FP8 there)."""
     td = lambda a: to_device(a, s, device)
-    return LayerWeights(
-        w_router=td(w_router),
-        bias=None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).to(device),
-        w_gate_up=pack(td(wgu)),
-        w_down=pack(td(wd)),
-        ws_gate_up=None if shared is None else pack(td(shared[0])),
-        ws_down=None if shared is None else pack(td(shared[1])),
-    )
+    router = td(w_router)
+    b = None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).to(device)
+    if not fp8:
+        return LayerWeights(
+            w_router=router, bias=b,
+            w_gate_up=pack(td(wgu)),
+            w_down=pack(td(wd)),
+            ws_gate_up=None if shared is None else pack(td(shared[0])),
+            ws_down=None if shared is None else pack(td(shared[1])),
+        )
+    gu, gus = quantize_fp8(td(wgu))
+    dn, dns = quantize_fp8(td(wd))
+    sgu = sgus = sdn = sdns = None
+    if shared is not None:
+        sgu, sgus = quantize_fp8(td(shared[0]))
+        sdn, sdns = quantize_fp8(td(shared[1]))
+    return LayerWeights(w_router=router, bias=b, w_gate_up=gu, w_down=dn, ws_gate_up=sgu,
+                        ws_down=sdn, fp8=True, w_gate_up_scale=gus, w_down_scale=dns,
+                        ws_gate_up_scale=sgus, ws_down_scale=sdns)
 
 
-def upload(inputs, device="cuda"):
+def upload(inputs, device="cuda", fp8: bool = False):
     """Seeded inputs (``inputs.LayerInputs``) -> (x, LayerWeights) on the device."""
     s = inputs.shape
     wgu, wd = inputs.all_experts()
-    w = upload_weights(s, inputs.w_router, inputs.bias, wgu, wd, inputs.shared(), device)
+    w = upload_weights(s, inputs.w_router, inputs.bias, wgu, wd, inputs.shared(), device, fp8)
     return to_device(inputs.x, s, device), w
 
 
@@ -273,8 +344,19 @@ def layer_forward(s: MoEShape, x: torch.Tensor, w: LayerWeights, b: LayerBuffers
     moe_route(c, x, w.w_router, w.bias, b.logits, b.topk_idx, b.topk_w, stream)
     moe_permute(c, b.topk_idx, x, b.counts, b.offsets, b.sorted_token, b.slot_of, b.x_perm,
                 b.workspace, stream)
-    moe_grouped_gate_up(c, b.x_perm, b.sorted_token, x, b.offsets, w.w_gate_up, w.ws_gate_up, b.h,
-                        stream)
-    moe_grouped_down(c, b.h, b.offsets, w.w_down, w.ws_down, b.y_perm, b.y_shared, stream)
+    grouped_ffn(c, x, w, b, stream)
     moe_combine(c, b.y_perm, b.y_shared, b.slot_of, b.topk_w, b.out, stream)
     return b.out
+
+
+def grouped_ffn(c: moe_shape, x: torch.Tensor, w: LayerWeights, b: LayerBuffers, stream=None):
+    """Both grouped GEMMs, with bf16 or FP8 expert weights."""
+    if w.fp8:
+        moe_grouped_gate_up_fp8(c, b.x_perm, b.sorted_token, x, b.offsets, w.w_gate_up,
+                                w.w_gate_up_scale, w.ws_gate_up, w.ws_gate_up_scale, b.h, stream)
+        moe_grouped_down_fp8(c, b.h, b.offsets, w.w_down, w.w_down_scale, w.ws_down, w.ws_down_scale,
+                             b.y_perm, b.y_shared, stream)
+    else:
+        moe_grouped_gate_up(c, b.x_perm, b.sorted_token, x, b.offsets, w.w_gate_up, w.ws_gate_up,
+                            b.h, stream)
+        moe_grouped_down(c, b.h, b.offsets, w.w_down, w.ws_down, b.y_perm, b.y_shared, stream)

@@ -247,6 +247,81 @@ int moe_pack_weights(const void* w, void* w_packed, int64_t count, int32_t rows,
   return launched(moe::launch_pack(w, w_packed, count, rows, cols, elem, as_stream(stream)));
 }
 
+size_t moe_fp8_packed_bytes(int64_t count, int32_t rows, int32_t cols) {
+  if (count < 0 || rows < 0 || cols < 0 || rows % 32 != 0 || cols % 32 != 0) return 0;
+  return static_cast<size_t>(count) * rows * cols;
+}
+
+int moe_quantize_weights_fp8(const void* w, void* w_fp8, float* scales, int64_t count, int32_t rows,
+                             int32_t cols, void* stream) {
+  if (count < 0 || rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "negative count or size");
+  if (rows % 32 != 0 || cols % 32 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "rows = %d and cols = %d must be multiples of 32", rows, cols);
+  if (count == 0 || rows == 0 || cols == 0) return ok();
+  NEED_PTR(w);
+  NEED_PTR(w_fp8);
+  NEED_PTR(scales);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(w_fp8),
+                  c = reinterpret_cast<uintptr_t>(scales);
+  const uintptr_t na = static_cast<uintptr_t>(count) * rows * cols * 2;
+  const uintptr_t nb = moe_fp8_packed_bytes(count, rows, cols);
+  const uintptr_t nc = static_cast<uintptr_t>(count) * rows * 4;
+  if ((a < b + nb && b < a + na) || (a < c + nc && c < a + na) || (b < c + nc && c < b + nb))
+    return fail(MOE_ERR_INVALID_ARG, "w, w_fp8 and scales overlap");
+  return launched(moe::launch_quantize_fp8(w, w_fp8, scales, count, rows, cols, as_stream(stream)));
+}
+
+int moe_grouped_gate_up_fp8(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
+                            const void* x, const int32_t* offsets, const void* w_gate_up,
+                            const float* w_gate_up_scale, const void* ws_gate_up,
+                            const float* ws_gate_up_scale, void* h, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (shape->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "FP8 weights need bf16 activations (dtype MOE_BF16)");
+  if (shape->T == 0) return ok();
+  OPT_PTR(x_perm);
+  if (x_perm == nullptr) NEED_PTR(sorted_token);
+  NEED_PTR(x);
+  NEED_PTR(offsets);
+  NEED_PTR(w_gate_up);
+  NEED_PTR(w_gate_up_scale);
+  if (shape->Fs > 0) {
+    NEED_PTR(ws_gate_up);
+    NEED_PTR(ws_gate_up_scale);
+  }
+  NEED_PTR(h);
+  const moe_shape& s = *shape;
+  return launched(moe::launch_gate_up_fp8(
+      s, static_cast<const moe::bf16_t*>(x_perm), sorted_token, static_cast<const moe::bf16_t*>(x),
+      offsets, static_cast<const uint8_t*>(w_gate_up), w_gate_up_scale,
+      static_cast<const uint8_t*>(ws_gate_up), ws_gate_up_scale, static_cast<moe::bf16_t*>(h),
+      as_stream(stream)));
+}
+
+int moe_grouped_down_fp8(const moe_shape* shape, const void* h, const int32_t* offsets,
+                         const void* w_down, const float* w_down_scale, const void* ws_down,
+                         const float* ws_down_scale, void* y_perm, void* y_shared, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (shape->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "FP8 weights need bf16 activations (dtype MOE_BF16)");
+  if (shape->T == 0) return ok();
+  NEED_PTR(h);
+  NEED_PTR(offsets);
+  NEED_PTR(w_down);
+  NEED_PTR(w_down_scale);
+  NEED_PTR(y_perm);
+  if (shape->Fs > 0) {
+    NEED_PTR(ws_down);
+    NEED_PTR(ws_down_scale);
+    NEED_PTR(y_shared);
+  }
+  const moe_shape& s = *shape;
+  return launched(moe::launch_down_fp8(
+      s, static_cast<const moe::bf16_t*>(h), offsets, static_cast<const uint8_t*>(w_down),
+      w_down_scale, static_cast<const uint8_t*>(ws_down), ws_down_scale,
+      static_cast<moe::bf16_t*>(y_perm), static_cast<moe::bf16_t*>(y_shared), as_stream(stream)));
+}
+
 int moe_combine(const moe_shape* shape, const void* y_perm, const void* y_shared,
                 const int32_t* slot_of, const float* topk_w, void* out, void* stream) {
   if (int r = check_shape(shape)) return r;

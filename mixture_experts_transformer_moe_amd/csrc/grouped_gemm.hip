@@ -41,8 +41,10 @@ struct GemmArgs {
   const bf16_t* a_routed;   // [S, K] rows in expert order (x_perm or h), or x when gather != null
   const int32_t* gather;    // sorted_token (A row p = x[gather[p]]) or null
   const bf16_t* a_shared;   // [T, Ks]
-  const bf16_t* w_routed;   // E packed [Nw, K] matrices
-  const bf16_t* w_shared;   // packed [Nws, Ks]
+  const unsigned char* w_routed;   // E packed [Nw, K] matrices (bf16, or FP8 codes)
+  const unsigned char* w_shared;   // packed [Nws, Ks]
+  const float* s_routed;    // FP8 weights: per-row scales [E, Nw] (else unused)
+  const float* s_shared;    //   [Nws]
   bf16_t* out_routed;       // [S, N]
   bf16_t* out_shared;       // [T, Ns]
   const int32_t* offsets;   // [E + 1]
@@ -53,10 +55,12 @@ struct GemmArgs {
 };
 
 // Output side of one tile.
+template <int NB>
 struct TileOut {
-  bf16_t* out;      // element (row r of the tile, column c of its 256) at out + r * ld + c
+  bf16_t* out;      // element (row r of the tile, column c of the wave's) at out + r * ld + c
   int ld;
   int valid;        // rows of the tile that hold tokens
+  const float* scale[NB];   // FP8 weights: the row scales of the wave's weight blocks
 };
 
 // One kernel for both GEMMs: a tile is BM token rows of one group x 256 weight
@@ -65,9 +69,10 @@ struct TileOut {
 // (mma_stream.h).  Wave w holds the gate block and the up block of the same 32
 // columns, so SwiGLU is applied in registers; outputs go straight from
 // registers to memory, eight adjacent bf16 values (16 bytes) per lane and store.
-template <int MODE, int BM, int NB, int PF>
+template <int MODE, int BM, int NB, int PF, bool W8>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
-  using ST = StreamTile<BM, NB, PF>;
+  using ST = StreamTile<BM, NB, PF, W8>;
+  using TileOut = moe::TileOut<NB>;
   constexpr int MBW = ST::MBW;
   // output columns per tile: gate_up pairs NB / 2 gate blocks with the up
   // blocks of the same columns (32 NB / 2 columns per wave); down: 32 NB per wave
@@ -226,10 +231,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       }
       src.a_off[q] = (r * static_cast<uint32_t>(K) + static_cast<uint32_t>(col)) * 2u;
     }
-    // packed weights: the wave's two 32-row blocks
-    const bf16_t* wbase =
-        shared ? g.w_shared
-               : g.w_routed + static_cast<size_t>(grp) * packed_matrix_elems(MODE == kGateUp ? 2 * Nout : Nout, K);
+    // packed weights: the wave's 32-row blocks, 32 K bytes per row block and
+    // element byte (1 for FP8 codes, 2 for bf16)
+    constexpr int kWB = W8 ? 1 : 2;
+    const int Nw = MODE == kGateUp ? 2 * Nout : Nout;             // rows of one weight matrix
+    const unsigned char* wbase =
+        shared ? g.w_shared : g.w_routed + static_cast<size_t>(grp) * Nw * K * kWB;
+    const float* sbase = W8 ? (shared ? g.s_shared : g.s_routed + static_cast<size_t>(grp) * Nw) : nullptr;
     // the wave's weight block rows and its first output column
     const int col0 = n0 + kWaveCols * wave;
 #pragma unroll
@@ -238,7 +246,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       // the same columns; down: NB consecutive blocks
       const int wrow = MODE == kGateUp ? (j < NB / 2 ? col0 + 32 * j : Nout + col0 + 32 * (j - NB / 2))
                                        : col0 + 32 * j;
-      src.w[j] = wbase + static_cast<size_t>(wrow >> 5) * (K >> 4) * 512;
+      src.w[j] = wbase + static_cast<size_t>(wrow >> 5) * K * 32 * kWB;
+      o.scale[j] = W8 ? sbase + wrow : nullptr;
     }
     o.out = (shared ? g.out_shared + static_cast<size_t>(m0) * Nout
                     : g.out_routed + static_cast<size_t>(rb + m0) * Nout) + col0;
@@ -275,12 +284,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   for (int ti = pos; ti < total; ti += G) {
     const TileOut o = ocur;
     f32x16 acc[MBW][NB];
-    stream_tile<BM, NB, PF, kDefer ? 0 : kStores>(cur, nxt, [&]() {
+    // FP8: the row scales of the lane's 16 accumulator rows per weight block,
+    // loaded in the tile's last K blocks (ordinary loads: the epilogue's wait
+    // for them counts the loads issued after them)
+    float wsc[W8 ? NB : 1][16];
+    stream_tile<BM, NB, PF, W8, kDefer ? 0 : kStores>(cur, nxt, [&]() {
       if (ti + G >= total) return false;
       decode(ti + G, nxt, onxt);
       return true;
     }, [&](auto u_tag) {
       constexpr int u = decltype(u_tag)::value;
+      if constexpr (W8 && u == 0) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            // rows 8q + 4 (l / 32) + 0..3 of the block: registers 4q..4q+3
+            const float4 v = *reinterpret_cast<const float4*>(o.scale[j] + 8 * q + 4 * (lane >> 5));
+            wsc[j][4 * q] = v.x;
+            wsc[j][4 * q + 1] = v.y;
+            wsc[j][4 * q + 2] = v.z;
+            wsc[j][4 * q + 3] = v.w;
+          }
+      }
       if (kDefer && has_pend) {
 #pragma unroll
         for (int s_idx = u * kPer; s_idx < (u + 1) * kPer && s_idx < kStores; ++s_idx) store_pend(s_idx);
@@ -303,10 +329,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               if (MODE == kGateUp) {
-                const float gv = acc[m][j][4 * q + e], uv = acc[m][j + NB / 2][4 * q + e];
+                float gv = acc[m][j][4 * q + e], uv = acc[m][j + NB / 2][4 * q + e];
+                if constexpr (W8) {
+                  gv *= wsc[j][4 * q + e];
+                  uv *= wsc[j + NB / 2][4 * q + e];
+                }
                 y[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
               } else {
                 y[e] = acc[m][j][4 * q + e];
+                if constexpr (W8) y[e] *= wsc[j][4 * q + e];
               }
             }
             v[h][0] = pack_bf16x2(y[0], y[1]);
@@ -366,35 +397,32 @@ int persistent_grid() {
 // blocks with 4 weight blocks per wave (each A fragment read from LDS feeds 4
 // MFMAs) measured best among the shapes whose accumulators and weight ring fit
 // the registers, when the output width allows their wider tiles.
-template <int MODE>
+template <int MODE, bool W8>
 hipError_t launch_tiles(const GemmArgs& a, const moe_shape& s, hipStream_t st) {
+  // the weight ring's depth: 16 K steps of bf16 weights, 8 ring steps (16 K
+  // steps) of FP8 ones
+  constexpr int P = W8 ? 8 : 16;
   const int mean_rows = (s.T * s.k) / s.E;
   const int wide = MODE == kGateUp ? 256 : 512;            // output columns of an NB = 4 tile
   if (mean_rows >= 192 && a.N % wide == 0 && (!a.has_shared || a.Ns % wide == 0))
-    grouped_gemm_kernel<MODE, 96, 4, 8><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 96, 4, 8, W8><<<persistent_grid(), kThreads, 0, st>>>(a);
   else if (mean_rows >= 96)
-    grouped_gemm_kernel<MODE, 160, 2, 16><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 160, 2, P, W8><<<persistent_grid(), kThreads, 0, st>>>(a);
   else if (mean_rows >= 48)
-    grouped_gemm_kernel<MODE, 128, 2, 16><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 128, 2, P, W8><<<persistent_grid(), kThreads, 0, st>>>(a);
   else if (mean_rows >= 24)
-    grouped_gemm_kernel<MODE, 64, 2, 16><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 64, 2, P, W8><<<persistent_grid(), kThreads, 0, st>>>(a);
   else
-    grouped_gemm_kernel<MODE, 32, 2, 16><<<persistent_grid(), kThreads, 0, st>>>(a);
+    grouped_gemm_kernel<MODE, 32, 2, P, W8><<<persistent_grid(), kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gate_up_bf16(const moe_shape& s, const bf16_t* x_perm,
-                               const int32_t* sorted_token, const bf16_t* x,
-                               const int32_t* offsets, const bf16_t* wgu, const bf16_t* wsgu,
-                               bf16_t* h, hipStream_t st) {
-  GemmArgs a;
+GemmArgs gate_up_args(const moe_shape& s, const bf16_t* x_perm, const int32_t* sorted_token,
+                      const bf16_t* x, const int32_t* offsets, bf16_t* h) {
+  GemmArgs a{};
   a.a_routed = x_perm ? x_perm : x;
   a.gather = x_perm ? nullptr : sorted_token;
   a.a_shared = x;
-  a.w_routed = wgu;
-  a.w_shared = wsgu;
   a.out_routed = h;
   a.out_shared = h + static_cast<size_t>(s.T) * s.k * s.F;
   a.offsets = offsets;
@@ -406,18 +434,15 @@ hipError_t launch_gate_up_bf16(const moe_shape& s, const bf16_t* x_perm,
   a.N = s.F;
   a.Ns = s.Fs;
   a.has_shared = s.Fs > 0;
-  return launch_tiles<kGateUp>(a, s, st);
+  return a;
 }
 
-hipError_t launch_down_bf16(const moe_shape& s, const bf16_t* h, const int32_t* offsets,
-                            const bf16_t* wd, const bf16_t* wsd, bf16_t* y_perm,
-                            bf16_t* y_shared, hipStream_t st) {
-  GemmArgs a;
+GemmArgs down_args(const moe_shape& s, const bf16_t* h, const int32_t* offsets, bf16_t* y_perm,
+                   bf16_t* y_shared) {
+  GemmArgs a{};
   a.a_routed = h;
   a.gather = nullptr;
   a.a_shared = h + static_cast<size_t>(s.T) * s.k * s.F;
-  a.w_routed = wd;
-  a.w_shared = wsd;
   a.out_routed = y_perm;
   a.out_shared = y_shared;
   a.offsets = offsets;
@@ -429,7 +454,51 @@ hipError_t launch_down_bf16(const moe_shape& s, const bf16_t* h, const int32_t* 
   a.N = s.D;
   a.Ns = s.D;
   a.has_shared = s.Fs > 0;
-  return launch_tiles<kDown>(a, s, st);
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_gate_up_bf16(const moe_shape& s, const bf16_t* x_perm,
+                               const int32_t* sorted_token, const bf16_t* x,
+                               const int32_t* offsets, const bf16_t* wgu, const bf16_t* wsgu,
+                               bf16_t* h, hipStream_t st) {
+  GemmArgs a = gate_up_args(s, x_perm, sorted_token, x, offsets, h);
+  a.w_routed = reinterpret_cast<const unsigned char*>(wgu);
+  a.w_shared = reinterpret_cast<const unsigned char*>(wsgu);
+  return launch_tiles<kGateUp, false>(a, s, st);
+}
+
+hipError_t launch_down_bf16(const moe_shape& s, const bf16_t* h, const int32_t* offsets,
+                            const bf16_t* wd, const bf16_t* wsd, bf16_t* y_perm,
+                            bf16_t* y_shared, hipStream_t st) {
+  GemmArgs a = down_args(s, h, offsets, y_perm, y_shared);
+  a.w_routed = reinterpret_cast<const unsigned char*>(wd);
+  a.w_shared = reinterpret_cast<const unsigned char*>(wsd);
+  return launch_tiles<kDown, false>(a, s, st);
+}
+
+hipError_t launch_gate_up_fp8(const moe_shape& s, const bf16_t* x_perm, const int32_t* sorted_token,
+                              const bf16_t* x, const int32_t* offsets, const uint8_t* wgu,
+                              const float* sgu, const uint8_t* wsgu, const float* ssgu, bf16_t* h,
+                              hipStream_t st) {
+  GemmArgs a = gate_up_args(s, x_perm, sorted_token, x, offsets, h);
+  a.w_routed = wgu;
+  a.w_shared = wsgu;
+  a.s_routed = sgu;
+  a.s_shared = ssgu;
+  return launch_tiles<kGateUp, true>(a, s, st);
+}
+
+hipError_t launch_down_fp8(const moe_shape& s, const bf16_t* h, const int32_t* offsets,
+                           const uint8_t* wd, const float* sd, const uint8_t* wsd, const float* ssd,
+                           bf16_t* y_perm, bf16_t* y_shared, hipStream_t st) {
+  GemmArgs a = down_args(s, h, offsets, y_perm, y_shared);
+  a.w_routed = wd;
+  a.w_shared = wsd;
+  a.s_routed = sd;
+  a.s_shared = ssd;
+  return launch_tiles<kDown, true>(a, s, st);
 }
 
 }  // namespace moe

@@ -14,6 +14,10 @@
 //     blocks with whole-line 16-byte loads into a ring of PF steps (4, 8 or
 //     16) of registers -- register space is far larger than LDS, so many bytes are in
 //     flight per CU, which is what an HBM-bound stream needs.
+//   * FP8 weights (W8): one 1 KB load per block holds the E4M3 codes of two
+//     16-wide K steps (8 bytes per lane each, moe_quantize_weights_fp8's
+//     layout); they are widened to bf16 in registers (exact) just before their
+//     MFMAs, so a ring step covers 2 K steps instead of 1.
 //   * Token rows (gathered through the expert order, L2/MALL resident) move by
 //     direct global->LDS loads (global_load_lds_dwordx4) into a ring of NS
 //     stages of 64-wide K blocks; chunks are XOR-swizzled by row for
@@ -44,11 +48,19 @@ constexpr int kStreamBK = 64;        // K per LDS stage (4 MFMA steps)
 constexpr int kStreamNS = 4;         // LDS stages
 constexpr int kStreamKAlign = 256;   // every K is a multiple (4 blocks, PF <= 16 steps)
 
-template <int BM, int NB, int PF>
+// Ring steps (1 KB weight loads per block) per K block of 64: 4 for bf16
+// weights, 2 for FP8 ones.
+template <bool W8>
+constexpr int kRingPerBlock = W8 ? 2 : 4;
+
+template <int BM, int NB, int PF, bool W8 = false>
 struct StreamTile {
   static constexpr int MBW = BM / 32;             // token blocks (every wave covers all)
   static constexpr int kAElems = BM * kStreamBK;  // one LDS stage
-  static_assert((NB == 2 || NB == 4) && MBW >= 1 && MBW <= 8 && (PF == 4 || PF == 8 || PF == 16),
+  // the ring must fit in the last 4 blocks of a tile (they prefetch the next
+  // tile's first PF steps)
+  static_assert((NB == 2 || NB == 4) && MBW >= 1 && MBW <= 8 && (PF == 4 || PF == 8 || PF == 16) &&
+                    PF <= 4 * kRingPerBlock<W8>,
                 "tile shape");
 };
 
@@ -82,14 +94,14 @@ template <int BM, int NB>
 struct StreamSrc {
   const bf16_t* a_base;                 // token rows: this lane's chunk of group g
   uint32_t a_off[BM / 32];              //   at K = 0 is at a_base + a_off[g] bytes
-  const bf16_t* w[NB];                  // the wave's packed weight block rows
+  const unsigned char* w[NB];           // the wave's packed weight blocks (1 KB per ring step)
   int nkb;                              // K / 64, a multiple of 4
 };
 
-// Weight operand of block j for 16-wide K step `step`.
+// Weight load (1 KB) of block j for ring step `step`.
 template <int BM, int NB>
-__device__ __forceinline__ const bf16_t* stream_wstep(const StreamSrc<BM, NB>& s, int j, int step) {
-  return s.w[j] + step * 512;
+__device__ __forceinline__ const unsigned char* stream_wstep(const StreamSrc<BM, NB>& s, int j, int step) {
+  return s.w[j] + step * 1024;
 }
 
 // What stays in flight between tiles.
@@ -125,7 +137,7 @@ __device__ __forceinline__ void stream_start(const StreamSrc<BM, NB>& s, StreamS
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) ss.bq[p][j] = *reinterpret_cast<const u32x4*>(stream_wstep(s, j, p) + lane * 8);
+    for (int j = 0; j < NB; ++j) ss.bq[p][j] = *reinterpret_cast<const u32x4*>(stream_wstep(s, j, p) + lane * 16);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -152,13 +164,23 @@ __device__ __forceinline__ void stream_read_a(const bf16_t* As, int ch, bf16x8 (
 
 // One MFMA step: NB MFMAs per token block.
 template <int MBW, int NB>
-__device__ __forceinline__ void stream_mfma(const bf16x8 (&fa)[MBW], const u32x4 (&bw)[NB],
+__device__ __forceinline__ void stream_mfma(const bf16x8 (&fa)[MBW], const bf16x8 (&bw)[NB],
                                             f32x16 (&acc)[MBW][NB]) {
 #pragma unroll
   for (int m = 0; m < MBW; ++m)
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      acc[m][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bw[j]), fa[m], acc[m][j], 0, 0, 0);
+      acc[m][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[j], fa[m], acc[m][j], 0, 0, 0);
+}
+
+// Eight E4M3 codes (two dwords, byte i = K element i) -> the bf16 MFMA operand
+// (exact: every E4M3 value is a bf16 value; scale 1).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t d0, uint32_t d1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // The K loop of one tile.  Every tile computes and loads all MBW token blocks
@@ -184,18 +206,20 @@ __device__ __forceinline__ void stream_mfma(const bf16x8 (&fa)[MBW], const u32x4
 // retire in issue order (loads and stores alike), so a wait that counts them
 // still guarantees its stage has landed and no longer drains the loads issued
 // after it.  A count past the counter's range falls back to the plain wait.
-template <int BM, int NB, int PF, int ST, typename Next, typename Hook>
+template <int BM, int NB, int PF, bool W8, int ST, typename Next, typename Hook>
 __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, StreamSrc<BM, NB>& nxt, Next&& next,
                                             Hook&& tail_hook, StreamState<NB, PF>& ss, const bf16_t* lds,
                                             f32x16 (&acc)[BM / 32][NB], bool stored) {
   constexpr int NS = kStreamNS;
   constexpr int MBW = BM / 32;
-  constexpr int U = PF / 4;                          // blocks per unrolled body
-  static_assert(NS == 4 && (PF == 16 || PF == 8 || PF == 4), "the schedule below is written for 4 stages");
-  // loads a wave issues per K block: MBW LDS loads and 4 NB weight loads.  The
-  // stage of block kb was issued 3 blocks earlier; after it came 3 x 4 NB
+  constexpr int RSB = kRingPerBlock<W8>;             // ring steps per K block
+  constexpr int U = PF / RSB;                        // blocks per unrolled body
+  static_assert(NS == 4 && StreamTile<BM, NB, PF, W8>::MBW == MBW && U >= 1 && PF % RSB == 0,
+                "the schedule below is written for 4 stages");
+  // loads a wave issues per K block: MBW LDS loads and RSB NB weight loads.
+  // The stage of block kb was issued 3 blocks earlier; after it came 3 x RSB NB
   // weight loads and the MBW LDS loads of 2 later stages.
-  constexpr int kW = 4 * NB * (NS - 1);
+  constexpr int kW = RSB * NB * (NS - 1);
   constexpr int kKeep = kW + 2 * MBW;
   static_assert(kKeep < 64, "vmcnt range");
   constexpr int kStoreComp = kKeep + ST <= 63 ? ST : 0;   // added to the waits of blocks 0..2
@@ -206,12 +230,13 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[m][j] = f32x16{0.f};
   bool has_next = false;
-  const bf16_t* tail_w[NB];
+  const unsigned char* tail_w[NB];
   int tail_stride = 0;
 #pragma unroll
   for (int j = 0; j < NB; ++j) tail_w[j] = cur.w[j];
 
-  // u: position of the block in its unrolled group (ring slots 4u..4u+3 mod PF)
+  // u: position of the block in its unrolled group (ring slots RSB u .. RSB u +
+  // RSB - 1 mod PF)
   auto kblock = [&](int kb, auto u_tag, auto last_tag) {
     constexpr int u = decltype(u_tag)::value;
     constexpr bool last = decltype(last_tag)::value; // u-th of the tile's last 4 blocks
@@ -251,20 +276,38 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
     }
     if constexpr (last) tail_hook(u_tag);
     const bf16_t* As = lds + ss.st * (BM * kStreamBK);
+    bf16x8 w8op[NB][2];                                // W8: the two K steps of a ring step
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int slot = (4 * u + i) % PF;             // == (4 kb + i) mod PF
+      const int rs = W8 ? i >> 1 : i;                  // ring step inside the block
+      const int slot = (RSB * u + rs) % PF;            // == (RSB kb + rs) mod PF
       bf16x8 fa[MBW];
       stream_read_a<MBW>(As, 2 * i + (lane >> 5), fa);
-      stream_mfma<MBW, NB>(fa, ss.bq[slot], acc);
-      // the step PF ahead: this tile's, or in the last blocks past its end the
-      // next tile's (every tile has at least 16 steps)
-      const bool from_next = last && (4 * u + i + PF >= 16);
+      bf16x8 bw[NB];
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const bf16_t* src = from_next ? tail_w[j] + (4 * u + i + PF - 16) * tail_stride
-                                      : stream_wstep(cur, j, 4 * kb + i + PF);
-        ss.bq[slot][j] = *reinterpret_cast<const u32x4*>(src + lane * 8);
+        if constexpr (W8) {
+          if ((i & 1) == 0) {
+            w8op[j][0] = fp8x8_to_bf16x8(ss.bq[slot][j][0], ss.bq[slot][j][1]);
+            w8op[j][1] = fp8x8_to_bf16x8(ss.bq[slot][j][2], ss.bq[slot][j][3]);
+          }
+          bw[j] = w8op[j][i & 1];
+        } else {
+          bw[j] = __builtin_bit_cast(bf16x8, ss.bq[slot][j]);
+        }
+      }
+      stream_mfma<MBW, NB>(fa, bw, acc);
+      // the ring step PF ahead, once this one's registers are free: this
+      // tile's, or in the last blocks past its end the next tile's (every
+      // tile has at least 4 RSB ring steps)
+      if (!W8 || (i & 1) == 1) {
+        const bool from_next = last && (RSB * u + rs + PF >= 4 * RSB);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const unsigned char* src = from_next ? tail_w[j] + (RSB * u + rs + PF - 4 * RSB) * tail_stride
+                                               : stream_wstep(cur, j, RSB * kb + rs + PF);
+          ss.bq[slot][j] = *reinterpret_cast<const u32x4*>(src + lane * 16);
+        }
       }
       // keep each refill right after the step that frees its registers: the
       // scheduler would otherwise sink the loads and shorten the prefetch
@@ -292,7 +335,7 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
   has_next = next();
 #pragma unroll
   for (int j = 0; j < NB; ++j) tail_w[j] = has_next ? nxt.w[j] : cur.w[j];
-  tail_stride = has_next ? 512 : 0;
+  tail_stride = has_next ? 1024 : 0;
   kblock(kb, I0{}, Yes{});
   kblock(kb + 1, I1{}, Yes{});
   kblock(kb + 2, I2{}, Yes{});

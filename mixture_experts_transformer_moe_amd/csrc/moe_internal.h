@@ -75,6 +75,15 @@ __host__ __device__ __forceinline__ size_t packed_offset(int row, int k, int K) 
   return blk * 512 + ((row & 31) + 32 * ((k >> 3) & 1)) * 8 + (k & 7);
 }
 
+hipError_t launch_quantize_fp8(const void* src, void* dst, float* scales, int64_t count, int rows,
+                               int cols, hipStream_t st);
+hipError_t launch_gate_up_fp8(const moe_shape& s, const bf16_t* x_perm, const int32_t* sorted_token,
+                              const bf16_t* x, const int32_t* offsets, const uint8_t* wgu,
+                              const float* sgu, const uint8_t* wsgu, const float* ssgu, bf16_t* h,
+                              hipStream_t st);
+hipError_t launch_down_fp8(const moe_shape& s, const bf16_t* h, const int32_t* offsets,
+                           const uint8_t* wd, const float* sd, const uint8_t* wsd, const float* ssd,
+                           bf16_t* y_perm, bf16_t* y_shared, hipStream_t st);
 hipError_t launch_pack(const void* src, void* dst, int64_t count, int rows, int cols, int elem,
                        hipStream_t st);
 

@@ -36,9 +36,10 @@ class StackedInputs:
         return self._shared
 
 
-def upload_stacked(inp: StackedInputs, device="cuda"):
+def upload_stacked(inp: StackedInputs, device="cuda", fp8: bool = False):
     s = inp.shape
-    w = binding.upload_weights(s, inp.w_router, inp.bias, inp.wgu, inp.wd, inp.shared(), device)
+    w = binding.upload_weights(s, inp.w_router, inp.bias, inp.wgu, inp.wd, inp.shared(), device,
+                               fp8=fp8)
     return binding.to_device(inp.x, s, device), w
 
 
@@ -46,9 +47,9 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_layer(s, inp: StackedInputs, gather: bool = False):
-    say(f"layer {s.name} T={s.T} D={s.D} E={s.E} k={s.k} F={s.F} Fs={s.Fs} gather={gather}")
-    x, w = upload_stacked(inp)
+def run_layer(s, inp: StackedInputs, gather: bool = False, fp8: bool = False):
+    say(f"layer {s.name} T={s.T} D={s.D} E={s.E} k={s.k} F={s.F} Fs={s.Fs} gather={gather} fp8={fp8}")
+    x, w = upload_stacked(inp, fp8=fp8)
     b = binding.alloc_buffers(s, with_x_perm=not gather)
     binding.layer_forward(s, x, w, b)
     torch.cuda.synchronize()

@@ -23,7 +23,7 @@ def L():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_and_binding_agree():
@@ -123,3 +123,28 @@ def test_packed_sizes_and_pack_argument_checks(L):
                               None) == binding.MOE_ERR_INVALID_ARG
     assert b"overlap" in L.moe_last_error()
     assert L.moe_pack_weights(p, q, 0, 32, 16, binding.MOE_BF16, None) == binding.MOE_OK
+
+
+def test_fp8_sizes_and_argument_checks(L):
+    # one byte per weight; rows and columns in whole 32 x 32 blocks
+    assert L.moe_fp8_packed_bytes(256, 2048, 4096) == 256 * 2048 * 4096
+    assert L.moe_fp8_packed_bytes(1, 32, 32) == 1024
+    for bad in ((1, 33, 32), (1, 32, 48), (-1, 32, 32)):
+        assert L.moe_fp8_packed_bytes(*bad) == 0
+    p, q, r = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 34)
+    assert L.moe_quantize_weights_fp8(p, q, r, 1, 32, 48, None) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_weights_fp8(p, None, r, 1, 32, 32, None) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_weights_fp8(p, q, None, 1, 32, 32, None) == binding.MOE_ERR_INVALID_ARG
+    # the scales may not overlap the codes
+    assert L.moe_quantize_weights_fp8(p, q, ctypes.c_void_p((1 << 30) + 512), 1, 32, 32,
+                                      None) == binding.MOE_ERR_INVALID_ARG
+    assert b"overlap" in L.moe_last_error()
+    assert L.moe_quantize_weights_fp8(p, q, r, 0, 32, 32, None) == binding.MOE_OK
+    # FP8 weights need bf16 activations; the grouped GEMMs check before launching
+    s = binding.make_shape(configs.TINY_F32)
+    args = [ctypes.c_void_p(1 << 20)] * 8
+    assert L.moe_grouped_gate_up_fp8(ctypes.byref(s), None, *args, None) == binding.MOE_ERR_UNSUPPORTED
+    sb = binding.make_shape(configs.variant(configs.XS2_T4096, T=64))
+    assert L.moe_grouped_down_fp8(ctypes.byref(sb), *([ctypes.c_void_p(1 << 20)] * 3), None,
+                                  *([ctypes.c_void_p(1 << 20)] * 4), None) == binding.MOE_ERR_INVALID_ARG
+    assert b"w_down_scale" in L.moe_last_error()
