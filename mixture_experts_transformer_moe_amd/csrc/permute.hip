@@ -5,6 +5,7 @@
 // Two index kernels and one copy, all deterministic (integer work only; LDS
 // atomics count and set bits, which gives the same result in any order):
 //   hist    one block per 256 tokens: per-block expert histogram -> workspace
+//           (a batch of at most 256 tokens runs both in a single block)
 //   scatter one block per 256 tokens: from all the blocks' histograms, each
 //           block derives the per-expert totals, their exclusive scan over the
 //           experts and its own first position of each expert's tokens (block
@@ -110,6 +111,57 @@ __global__ __launch_bounds__(kTB) void perm_scatter_kernel(const int32_t* __rest
   }
 }
 
+// All of it in one block when the batch is one block of tokens (T <= 256,
+// decode-sized): the histogram, the scan over the experts and the scatter,
+// without the workspace round trip and the second launch.
+__global__ __launch_bounds__(kTB) void perm_single_block_kernel(const int32_t* __restrict__ idx, int T,
+                                                                int E, int k, int S,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ sorted_token,
+                                                                int32_t* __restrict__ slot_of) {
+  __shared__ uint32_t chose[kMaxE][kTB / 32];   // bit t of row e: token t chose e
+  __shared__ int32_t hist[kMaxE];
+  __shared__ int32_t scan[kMaxE];
+  const int t = threadIdx.x;                      // token, and expert for the scan
+  for (int i = t; i < kMaxE * (kTB / 32); i += kTB) (&chose[0][0])[i] = 0u;
+  hist[t] = 0;
+  __syncthreads();
+  const int word = t >> 5;
+  const uint32_t bit = 1u << (t & 31);
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      const int e = clamp_e(idx[static_cast<size_t>(t) * k + j], E);
+      atomicAdd(&hist[e], 1);
+      atomicOr(&chose[e][word], bit);
+    }
+  __syncthreads();
+  const int total = hist[t];
+  scan[t] = total;
+  __syncthreads();
+  for (int off = 1; off < kMaxE; off <<= 1) {
+    const int v = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
+  }
+  if (t < E) {
+    counts[t] = total;
+    offsets[t] = scan[t] - total;
+  }
+  if (t == 0) offsets[E] = S;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = clamp_e(idx[static_cast<size_t>(t) * k + j], E);
+      int rank = __popc(chose[e][word] & (bit - 1u));
+      for (int w = 0; w < word; ++w) rank += __popc(chose[e][w]);
+      const int pos = scan[e] - hist[e] + rank;
+      slot_of[static_cast<size_t>(t) * k + j] = pos;
+      sorted_token[pos] = t;
+    }
+  }
+}
+
 // Copies rows in 16-byte chunks; row_vec = chunks per row.
 __global__ __launch_bounds__(256) void perm_gather_kernel(const u32x4* __restrict__ x,
                                                           const int32_t* __restrict__ sorted_token,
@@ -153,10 +205,15 @@ hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x,
   int32_t* blk = static_cast<int32_t*>(workspace);
   const int S = s.T * s.k;
   hipError_t err;
-  perm_hist_kernel<<<nb, kTB, 0, st>>>(idx, s.T, s.E, s.k, blk);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  perm_scatter_kernel<<<nb, kTB, 0, st>>>(idx, s.T, s.E, s.k, nb, S, blk, counts, offsets,
-                                          sorted_token, slot_of);
+  if (nb == 1) {
+    perm_single_block_kernel<<<1, kTB, 0, st>>>(idx, s.T, s.E, s.k, S, counts, offsets,
+                                                sorted_token, slot_of);
+  } else {
+    perm_hist_kernel<<<nb, kTB, 0, st>>>(idx, s.T, s.E, s.k, blk);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    perm_scatter_kernel<<<nb, kTB, 0, st>>>(idx, s.T, s.E, s.k, nb, S, blk, counts, offsets,
+                                            sorted_token, slot_of);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (x_perm) {
     const int elem = s.dtype == MOE_BF16 ? 2 : 4;

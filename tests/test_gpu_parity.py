@@ -105,6 +105,8 @@ EDGE = {
     "E1_k1": dict(E=1, k=1),
     "no_shared": dict(Fs=0),
     "T1": dict(T=1),
+    "T256_one_block": dict(T=256),           # the permutation's single-block path, full
+    "T257_two_blocks": dict(T=257),          # two blocks, the second with one token
     "T33_wide_shared": dict(T=33, Fs=512),
     "E256_T70": dict(T=70, E=256, k=8),
     # tile shapes chosen by the mean rows per expert (k T / E)
