@@ -1,5 +1,6 @@
 // Grouped GEMMs of the routed experts and the shared expert, bf16 operands on
-// gfx950 MFMA with fp32 accumulation.
+// gfx950 MFMA with fp32 accumulation (FP8 weights are widened to bf16 in
+// registers and their row scales applied to the accumulators).
 //
 // What they compute ("Laguna-M.1-base", Feed-forward: SwiGLU without biases;
 // grouped GEMM over tokens in expert order, "Laguna M.1/XS.2 Technical Report",
@@ -19,13 +20,15 @@
 //     same L2, and every workgroup gets the same number of tiles to within
 //     one; the shared expert's row-block height is picked so that its tiles
 //     fill the last round (gate_up spreads them through all rounds instead);
-//   * BM x 256 tiles (BM by the mean rows per expert, so an expert's rows
-//     mostly fit one tile and its weights stream once), one workgroup per CU;
-//     weights, packed in MFMA fragment order, stream from HBM straight into
-//     registers through a deep prefetch ring, token rows go through an LDS ring
-//     (mma_stream.h); gate_up tiles pair each gate block with the up block of
-//     the same columns, so SwiGLU is applied in registers before one rounding
-//     to bf16, and results are stored straight from registers.
+//   * tiles of BM token rows x 256 or 512 weight rows (BM by the mean rows per
+//     expert, so an expert's rows mostly fit one tile and its weights stream
+//     once), one workgroup per CU; weights, packed in MFMA fragment order,
+//     stream from HBM straight into registers through a deep prefetch ring,
+//     token rows go through an LDS ring (mma_stream.h); gate_up tiles pair each
+//     gate block with the up block of the same columns, so SwiGLU is applied in
+//     registers before one rounding to bf16;
+//   * a tile's outputs are stored while the next tile's loads stream (see the
+//     epilogue), 16 bytes per lane after a lane-pair swap.
 #include "mma_stream.h"
 
 namespace moe {

@@ -30,12 +30,13 @@
 //     their waits are explicit and count exactly the loads issued after them;
 //     the register loads are ordinary loads whose waits the compiler derives.
 //   * Every tile loads and multiplies all BM rows (rows past its last one
-//     repeat it and their results are dropped): the per-block load counts are
-//     then the same for every tile, every wait is a constant, and one set of
-//     registers holds the weight ring for all tiles.
+//     repeat it, so their results repeat its results): the per-block load
+//     counts are then the same for every tile, every wait is a compile-time
+//     constant, and one set of registers holds the weight ring for all tiles.
 // The weight operand is the MFMA's first operand: in an accumulator lane l holds
 // token (l mod 32) of its block and register quad q four consecutive weight
-// rows, so epilogues store four adjacent outputs of one token at once.
+// rows; the epilogues pair lanes l and l + 32 so that each stores eight adjacent
+// outputs of one token.
 #pragma once
 
 #include <type_traits>
