@@ -92,3 +92,20 @@ def test_fp8_layer_parity(case):
 
 def test_fp8_decode_workload_full_parity():
     fp8_parity(configs.DECODE_SKEW_T32, gather=True)
+
+
+def test_quantize_writes_nothing_past_its_outputs():
+    rng = np.random.default_rng(9)
+    count, rows, cols = 2, 64, 96
+    bits = _bf16_bits(rng.normal(0, 0.02, (count, rows, cols)))
+    dev = binding.to_device(bits, SMALL, "cuda")
+    n_codes, n_scales, pad = count * rows * cols, count * rows, 4096
+    codes = torch.full((n_codes + pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full((n_scales + pad,), -7.0, dtype=torch.float32, device="cuda")
+    binding.moe_quantize_weights_fp8(dev, codes, scales, count, rows, cols)
+    torch.cuda.synchronize()
+    assert bool((codes[n_codes:] == 0xA5).all()), "write past the codes"
+    assert bool((scales[n_scales:] == -7.0).all()), "write past the scales"
+    ref_codes, ref_scales = F.quantize_rows(bits)
+    assert np.array_equal(_unpack_codes(codes[:n_codes].cpu().numpy(), count, rows, cols), ref_codes)
+    assert np.array_equal(scales[:n_scales].view(count, rows).cpu().numpy(), ref_scales)

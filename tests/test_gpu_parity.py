@@ -167,11 +167,12 @@ def _guard_intact(big: torch.Tensor, n: int) -> bool:
     return bool((ints == (0x5a5a if big.element_size() == 2 else 0x5a5a5a5a)).all())
 
 
-def test_determinism_and_no_out_of_bounds_writes():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_determinism_and_no_out_of_bounds_writes(fp8):
     s = SMALL_BF16
     inp = StackedInputs(LayerInputs(s))
     from tests.gpu_common import upload_stacked
-    x, w = upload_stacked(inp)
+    x, w = upload_stacked(inp, fp8=fp8)
     outs = []
     for rep in range(3):
         say(f"determinism rep {rep}")
