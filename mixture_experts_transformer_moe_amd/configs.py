@@ -39,6 +39,13 @@ class MoEShape:
     outlier_frac: float = 0.0          # share of tokens that carry outliers
     outlier_scale: float = 50.0
     outlier_channels: int = 8
+    # training pass: upstream gradient dout ~ N(0, dout_std^2); padding tokens
+    # at the tails of sequences of seq_len tokens, pad_frac of the batch on
+    # average; auxiliary load-balancing loss coefficient
+    dout_std: float = 1.0
+    pad_frac: float = 0.0
+    seq_len: int = 1024
+    aux_coef: float = 1e-3
 
     @property
     def S(self) -> int:

@@ -22,7 +22,12 @@ Recipes (per workload, see ``configs.MoEShape``):
     activation outliers are reported in the digg.com thread on the report,
     quantization item);
   * router bias "zipf": b_e = -s * ln(r_e) with r a seeded permutation of 1..E,
-    i.e. the log of a Zipf(s) popularity law, max-normalised to 0.
+    i.e. the log of a Zipf(s) popularity law, max-normalised to 0;
+  * training pass: the upstream gradient dout ~ N(0, dout_std^2) [T, D]; the
+    padding mask cuts the batch into sequences of seq_len tokens (the last one
+    may be shorter) and pads the tail of each, its length drawn uniformly from
+    0 .. 2 pad_frac seq_len, so pad_frac of the tokens are padding on average
+    (padded sequence ends, where a packed batch has them).
 """
 from __future__ import annotations
 
@@ -39,6 +44,7 @@ TID_X, TID_ROUTER, TID_BIAS = 0, 1, 2
 TID_GATE, TID_UP, TID_DOWN = 3, 4, 5
 TID_SGATE, TID_SUP, TID_SDOWN = 6, 7, 8
 TID_OUTLIER = 9
+TID_DOUT, TID_PAD = 10, 11
 
 
 def rng_for(seed: int, tensor_id: int, expert: int = 0) -> np.random.Generator:
@@ -103,6 +109,31 @@ def router_bias(shape: MoEShape) -> Optional[np.ndarray]:
         r = rng_for(shape.seed, TID_BIAS, 0).permutation(shape.E) + 1
         return (-np.float64(shape.zipf_s) * np.log(r.astype(np.float64))).astype(np.float32)
     raise ValueError(shape.bias)
+
+
+def dout_f32(shape: MoEShape) -> np.ndarray:
+    """Upstream gradient of the layer output, fp32 [T, D], before encoding."""
+    return _normal(shape.seed, TID_DOUT, 0, (shape.T, shape.D), shape.dout_std)
+
+
+def dout_encoded(shape: MoEShape) -> np.ndarray:
+    return _encode(shape, dout_f32(shape))
+
+
+def token_mask(shape: MoEShape) -> np.ndarray:
+    """uint8 [T]: 1 for a real token, 0 for padding (all 1 when pad_frac is 0)."""
+    T = shape.T
+    mask = np.ones(T, dtype=np.uint8)
+    if shape.pad_frac <= 0 or T == 0:
+        return mask
+    g = rng_for(shape.seed, TID_PAD, 0)
+    L = max(1, shape.seq_len)
+    top = int(round(2 * shape.pad_frac * L))
+    for start in range(0, T, L):
+        end = min(start + L, T)
+        n_pad = min(int(g.integers(0, top + 1)), end - start)
+        mask[end - n_pad:end] = 0
+    return mask
 
 
 class LayerInputs:
