@@ -101,16 +101,31 @@ size_t moe_workspace_bytes(const moe_shape* shape);
 int moe_route(const moe_shape* shape, const void* x, const void* w_router, const float* bias,
               float* logits, int32_t* topk_idx, float* topk_w, void* stream);
 
+/* moe_route with a padding mask: padding tokens are neither routed nor load
+ * balanced ("Laguna M.1/XS.2 Technical Report", thread on the report: padding
+ * tokens always went to one expert and could not learn, so they were left out
+ * of routing and load balancing).
+ *   mask      [T] uint8 or NULL (= every token routed); 0 marks padding
+ * A padding token's logits are still written; its topk_idx row is -1 and its
+ * topk_w row 0.  moe_permute and moe_combine then skip it: its output is the
+ * shared expert's alone. */
+int moe_route_masked(const moe_shape* shape, const void* x, const void* w_router, const float* bias,
+                     const uint8_t* mask, float* logits, int32_t* topk_idx, float* topk_w,
+                     void* stream);
+
 /* Expert-order permutation: the on-device form of the dispatch all-to-all
  * (tokens copied "in expert order": "Laguna M.1/XS.2 Technical Report", Key
  * claims, fused dispatch/grouped GEMM, report section 3.1.2, Fig. 2).
- *   topk_idx     [T, k] int32   in: from moe_route (values must lie in [0, E))
+ *   topk_idx     [T, k] int32   in: from moe_route (values in [0, E)) or
+ *                               moe_route_masked (-1: a slot not routed)
  *   x            [T, D] elem    in: layer input
  *   counts       [E] int32      out: tokens routed to each expert
- *   offsets      [E+1] int32    out: exclusive scan of counts, offsets[E] = k*T
+ *   offsets      [E+1] int32    out: exclusive scan of counts; offsets[E] = the
+ *                               routed slots (k*T without padding)
  *   sorted_token [k*T] int32    out: expert by expert, the tokens in ascending
- *                               token order
- *   slot_of      [T, k] int32   out: position of (t, j) in that order
+ *                               token order (the first offsets[E] entries)
+ *   slot_of      [T, k] int32   out: position of (t, j) in that order; -1 for a
+ *                               slot not routed
  *   x_perm       [k*T, D] elem  out: x_perm[p] = x[sorted_token[p]]; may be NULL
  *                               to skip the copy
  *   workspace    >= moe_workspace_bytes(shape) bytes, caller-owned scratch
@@ -238,10 +253,118 @@ int moe_grouped_down_fp8(const moe_shape* shape, const void* h, const int32_t* o
  * Technical Report", Key claims: routed output modulated by alpha before
  * combining with the shared expert).
  *   y_perm    [k*T, D] elem;  y_shared [T, D] elem or NULL (no shared expert)
- *   slot_of   [T, k] int32;   topk_w [T, k] fp32
+ *   slot_of   [T, k] int32 (slots < 0 are skipped);   topk_w [T, k] fp32
  *   out       [T, D] elem out */
 int moe_combine(const moe_shape* shape, const void* y_perm, const void* y_shared,
                 const int32_t* slot_of, const float* topk_w, void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Training pass (MOE_BF16 only; MOE_ERR_UNSUPPORTED otherwise).
+ *
+ * Forward: moe_route_masked, moe_permute, moe_load_stats,
+ * moe_grouped_gate_up_train, moe_grouped_down, moe_combine.  Backward of
+ *   J = <dout, out> + L_aux
+ * with the top-k selection held fixed: moe_combine_backward,
+ * moe_grouped_backward_h, moe_grouped_backward_x, moe_weight_grads.
+ * Readings (the pages state none of these formulas):
+ *   - load balancing is the global-batch auxiliary loss of Qiu et al. ("Laguna
+ *     M.1/XS.2 Technical Report", Key claims, XS.2 routing item): over the N
+ *     routed tokens of this batch, f_e = counts_e / sum counts (counts of the
+ *     GLOBAL batch: the caller's sum over micro-batches and ranks, or this
+ *     batch's), p_e = mean of sigmoid(z_te) / sum_e' sigmoid(z_te'),
+ *     L_aux = beta * E * sum_e f_e p_e; the gradient flows through p only;
+ *   - weight gradients are bf16 for the experts (bf16 mixed precision: report,
+ *     Key claims, report section 3.1.1), fp32 for the router and its bias.
+ * Packed transposed weights (moe_pack_weights_transposed) serve the backward
+ * products: w_down_t = W_d^T [E, F, D] (k_padded = D), w_gate_up_t =
+ * [W_g; W_u]^T [E, D, 2F] (k_padded = 2F), the shared ones alike, and
+ * w_router_t = W_r^T [D, 256] (k_padded = 256: rows of W_r past E are zero).
+ * Buffers below: S = k*T; "routed + shared" buffers hold the S routed rows in
+ * expert order, then the T shared rows.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of workspace moe_load_stats and moe_weight_grads (bias gradient) need. */
+size_t moe_train_workspace_bytes(const moe_shape* shape);
+
+/* Bytes of moe_pack_weights_transposed's output: count * cols * k_padded * 2,
+ * or 0 for a shape it rejects. */
+size_t moe_packed_transposed_bytes(int64_t count, int32_t rows, int32_t cols, int32_t k_padded);
+
+/* Transposed packing: matrix i of w [count, rows, cols] bf16 becomes its
+ * transpose [cols, k_padded], packed like moe_pack_weights, with columns
+ * k >= rows of the transpose zero.  cols % 32 == 0, k_padded % 16 == 0,
+ * k_padded >= rows (else MOE_ERR_INVALID_ARG); w_packed must not overlap w. */
+int moe_pack_weights_transposed(const void* w, void* w_packed, int64_t count, int32_t rows, int32_t cols,
+                                int32_t k_padded, void* stream);
+
+/* Load statistics and auxiliary loss.
+ *   logits, topk_idx   from moe_route_masked (topk_idx[t, 0] < 0: padding)
+ *   counts [E] int32   this batch's counts (moe_permute); N = sum counts / k
+ *   counts_global [E] int32 or NULL: the global batch's counts (NULL = counts)
+ *   beta               auxiliary-loss coefficient (not disclosed by the pages)
+ *   f, p [E] fp32 out; aux_loss [1] fp32 out;
+ *   aux_coef [E] fp32 out: beta * E * f / N, the input of moe_combine_backward
+ *   workspace >= moe_train_workspace_bytes
+ * Sums run in a fixed order: the results are bit-reproducible. */
+int moe_load_stats(const moe_shape* shape, const float* logits, const int32_t* topk_idx,
+                   const int32_t* counts, const int32_t* counts_global, float beta, float* f, float* p,
+                   float* aux_loss, float* aux_coef, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Forward gate/up for training: the pre-activations and the SwiGLU output.
+ *   arguments as moe_grouped_gate_up (w_gate_up packed by moe_pack_weights)
+ *   gu  [S, 2F] + [T, 2Fs] bf16 out: [g | u] of each routed row, then of the
+ *       shared expert (rounded to bf16)
+ *   h   [S, F] + [T, Fs] bf16 out: silu(g) * u from those bf16 values */
+int moe_grouped_gate_up_train(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
+                              const void* x, const int32_t* offsets, const void* w_gate_up,
+                              const void* ws_gate_up, void* gu, void* h, void* stream);
+
+/* Backward of the combine, the renormalisation, the sigmoid and L_aux.
+ *   dout [T, D] bf16; y_perm, slot_of, topk_idx, topk_w, logits from the forward
+ *   aux_coef [E] fp32 from moe_load_stats, or NULL (no auxiliary loss)
+ *   dy_perm [S, D] bf16 out: alpha * w_{t,j} * dout_t at row slot_of[t, j]
+ *   dz [T, E] fp32 out: dJ/dz (zero rows for padding)
+ *   dz_bf16 [T, 256] bf16 out: the same, rounded, zero past column E */
+int moe_combine_backward(const moe_shape* shape, const void* dout, const void* y_perm,
+                         const int32_t* slot_of, const int32_t* topk_idx, const float* topk_w,
+                         const float* logits, const float* aux_coef, void* dy_perm, float* dz,
+                         void* dz_bf16, void* stream);
+
+/* dh = dy W_d per expert (the shared expert's dy is dout), then the SwiGLU
+ * backward dg = dh u silu'(g), du = dh silu(g).
+ *   w_down_t [E, F, D], ws_down_t [Fs, D]: packed transposed down weights
+ *   gu from moe_grouped_gate_up_train
+ *   dh [S, F] + [T, Fs] bf16 out (intermediate); dgu [S, 2F] + [T, 2Fs] bf16 out */
+int moe_grouped_backward_h(const moe_shape* shape, const void* dy_perm, const void* dout,
+                           const int32_t* offsets, const void* w_down_t, const void* ws_down_t,
+                           const void* gu, void* dh, void* dgu, void* stream);
+
+/* Input gradient: dx_perm = [dg | du] [W_g; W_u] per routed row, dx_shared the
+ * same for the shared expert, dx_router = dz W_r, then
+ *   dx_t = dx_shared_t + dx_router_t + sum over t's routed slots of dx_perm rows.
+ *   w_gate_up_t [E, D, 2F], ws_gate_up_t [D, 2Fs], w_router_t [D, 256]: packed
+ *   transposed; dx_perm [S, D], dx_shared [T, D] (unused when Fs == 0),
+ *   dx_router [T, D], dx [T, D]: bf16 out */
+int moe_grouped_backward_x(const moe_shape* shape, const void* dgu, const int32_t* offsets,
+                           const void* w_gate_up_t, const void* ws_gate_up_t, const void* dz_bf16,
+                           const void* w_router_t, const int32_t* slot_of, void* dx_perm, void* dx_shared,
+                           void* dx_router, void* dx, void* stream);
+
+/* Weight gradients, each a sum over the group's token rows (zero for an expert
+ * without rows; T == 0 writes zeros and reads no input):
+ *   dw_gate_up [E, 2F, D] bf16 = [dg | du]^T x of the expert's rows
+ *   dw_down    [E, D, F]  bf16 = dy^T h
+ *   dws_gate_up [2Fs, D], dws_down [D, Fs] bf16: the shared expert over all T
+ *              rows (dy = dout); unused when Fs == 0
+ *   dw_router  [E, D] fp32 = dz^T x, or NULL to skip
+ *   dbias      [E] fp32 = sum_t dz_t, or NULL to skip (needs the workspace)
+ *   x_perm may be NULL (rows then come from x through sorted_token). */
+int moe_weight_grads(const moe_shape* shape, const void* x, const int32_t* sorted_token,
+                     const void* x_perm, const int32_t* offsets, const void* dgu, const void* dy_perm,
+                     const void* dout, const void* h, const void* dz_bf16, const float* dz,
+                     void* dw_gate_up, void* dw_down, void* dws_gate_up, void* dws_down, float* dw_router,
+                     float* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,11 @@ MOE_F32, MOE_BF16 = 0, 1
 EXPORTS = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
            "moe_route", "moe_permute", "moe_pack_weights", "moe_packed_bytes", "moe_grouped_gate_up",
            "moe_grouped_down", "moe_grouped_ffn", "moe_fp8_packed_bytes", "moe_quantize_weights_fp8",
-           "moe_grouped_gate_up_fp8", "moe_grouped_down_fp8", "moe_combine")
+           "moe_grouped_gate_up_fp8", "moe_grouped_down_fp8", "moe_combine",
+           "moe_route_masked", "moe_train_workspace_bytes", "moe_packed_transposed_bytes",
+           "moe_pack_weights_transposed", "moe_load_stats", "moe_grouped_gate_up_train",
+           "moe_combine_backward", "moe_grouped_backward_h", "moe_grouped_backward_x",
+           "moe_weight_grads")
 
 
 class moe_shape(ctypes.Structure):
@@ -89,6 +93,30 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_down_fp8.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine.argtypes = [_SP, _P, _P, _P, _P, _P, _P]
+        # training pass
+        L.moe_route_masked.restype = ctypes.c_int
+        L.moe_route_masked.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_train_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_train_workspace_bytes.argtypes = [_SP]
+        L.moe_packed_transposed_bytes.restype = ctypes.c_size_t
+        L.moe_packed_transposed_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.c_int32]
+        L.moe_pack_weights_transposed.restype = ctypes.c_int
+        L.moe_pack_weights_transposed.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32,
+                                                  ctypes.c_int32, ctypes.c_int32, _P]
+        L.moe_load_stats.restype = ctypes.c_int
+        L.moe_load_stats.argtypes = [_SP, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P,
+                                     ctypes.c_size_t, _P]
+        L.moe_grouped_gate_up_train.restype = ctypes.c_int
+        L.moe_grouped_gate_up_train.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_combine_backward.restype = ctypes.c_int
+        L.moe_combine_backward.argtypes = [_SP] + [_P] * 11
+        L.moe_grouped_backward_h.restype = ctypes.c_int
+        L.moe_grouped_backward_h.argtypes = [_SP] + [_P] * 9
+        L.moe_grouped_backward_x.restype = ctypes.c_int
+        L.moe_grouped_backward_x.argtypes = [_SP] + [_P] * 12
+        L.moe_weight_grads.restype = ctypes.c_int
+        L.moe_weight_grads.argtypes = [_SP] + [_P] * 17 + [ctypes.c_size_t, _P]
         _lib = L
     return _lib
 
@@ -360,3 +388,206 @@ def grouped_ffn(c: moe_shape, x: torch.Tensor, w: LayerWeights, b: LayerBuffers,
         moe_grouped_gate_up(c, b.x_perm, b.sorted_token, x, b.offsets, w.w_gate_up, w.ws_gate_up,
                             b.h, stream)
         moe_grouped_down(c, b.h, b.offsets, w.w_down, w.ws_down, b.y_perm, b.y_shared, stream)
+
+
+# ---------------------------------------------------------------------------
+# training pass
+# ---------------------------------------------------------------------------
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def moe_route_masked(shape, x, w_router, bias, mask, logits, topk_idx, topk_w, stream=None):
+    _check(lib().moe_route_masked(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(mask),
+                                  _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
+           "moe_route_masked")
+
+
+def train_workspace_bytes(shape: moe_shape) -> int:
+    return int(lib().moe_train_workspace_bytes(ctypes.byref(shape)))
+
+
+def moe_packed_transposed_bytes(count, rows, cols, k_padded) -> int:
+    return int(lib().moe_packed_transposed_bytes(int(count), int(rows), int(cols), int(k_padded)))
+
+
+def moe_pack_weights_transposed(w, w_packed, count, rows, cols, k_padded, stream=None):
+    _check(lib().moe_pack_weights_transposed(_ptr(w), _ptr(w_packed), int(count), int(rows), int(cols),
+                                             int(k_padded), _stream(stream)), "moe_pack_weights_transposed")
+
+
+def pack_transposed(w: torch.Tensor, k_padded: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Packed transposes of a bf16 [rows, cols] or [count, rows, cols] tensor
+    (flat bf16 tensor of moe_packed_transposed_bytes bytes)."""
+    if w.dim() == 2:
+        count, rows, cols = 1, w.shape[0], w.shape[1]
+    else:
+        count, rows, cols = w.shape
+    kp = rows if k_padded is None else k_padded
+    nbytes = moe_packed_transposed_bytes(count, rows, cols, kp)
+    if nbytes == 0 and count * cols * kp > 0:
+        raise MoEError(MOE_ERR_INVALID_ARG, f"cannot pack the transpose of [{count}, {rows}, {cols}]")
+    out = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=w.device)
+    moe_pack_weights_transposed(w.contiguous(), out, count, rows, cols, kp, stream)
+    return out
+
+
+def moe_load_stats(shape, logits, topk_idx, counts, counts_global, beta, f, p, aux_loss, aux_coef,
+                   workspace, stream=None):
+    _check(lib().moe_load_stats(ctypes.byref(shape), _ptr(logits), _ptr(topk_idx), _ptr(counts),
+                                _ptr(counts_global), float(beta), _ptr(f), _ptr(p), _ptr(aux_loss),
+                                _ptr(aux_coef), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "moe_load_stats")
+
+
+def moe_grouped_gate_up_train(shape, x_perm, sorted_token, x, offsets, w_gate_up, ws_gate_up, gu, h,
+                              stream=None):
+    _check(lib().moe_grouped_gate_up_train(ctypes.byref(shape), _ptr(x_perm), _ptr(sorted_token), _ptr(x),
+                                           _ptr(offsets), _ptr(w_gate_up), _ptr(ws_gate_up), _ptr(gu),
+                                           _ptr(h), _stream(stream)), "moe_grouped_gate_up_train")
+
+
+def moe_combine_backward(shape, dout, y_perm, slot_of, topk_idx, topk_w, logits, aux_coef, dy_perm, dz,
+                         dz_bf16, stream=None):
+    _check(lib().moe_combine_backward(ctypes.byref(shape), _ptr(dout), _ptr(y_perm), _ptr(slot_of),
+                                      _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(aux_coef),
+                                      _ptr(dy_perm), _ptr(dz), _ptr(dz_bf16), _stream(stream)),
+           "moe_combine_backward")
+
+
+def moe_grouped_backward_h(shape, dy_perm, dout, offsets, w_down_t, ws_down_t, gu, dh, dgu, stream=None):
+    _check(lib().moe_grouped_backward_h(ctypes.byref(shape), _ptr(dy_perm), _ptr(dout), _ptr(offsets),
+                                        _ptr(w_down_t), _ptr(ws_down_t), _ptr(gu), _ptr(dh), _ptr(dgu),
+                                        _stream(stream)), "moe_grouped_backward_h")
+
+
+def moe_grouped_backward_x(shape, dgu, offsets, w_gate_up_t, ws_gate_up_t, dz_bf16, w_router_t, slot_of,
+                           dx_perm, dx_shared, dx_router, dx, stream=None):
+    _check(lib().moe_grouped_backward_x(ctypes.byref(shape), _ptr(dgu), _ptr(offsets), _ptr(w_gate_up_t),
+                                        _ptr(ws_gate_up_t), _ptr(dz_bf16), _ptr(w_router_t), _ptr(slot_of),
+                                        _ptr(dx_perm), _ptr(dx_shared), _ptr(dx_router), _ptr(dx),
+                                        _stream(stream)), "moe_grouped_backward_x")
+
+
+def moe_weight_grads(shape, x, sorted_token, x_perm, offsets, dgu, dy_perm, dout, h, dz_bf16, dz,
+                     dw_gate_up, dw_down, dws_gate_up, dws_down, dw_router, dbias, workspace,
+                     stream=None):
+    _check(lib().moe_weight_grads(ctypes.byref(shape), _ptr(x), _ptr(sorted_token), _ptr(x_perm),
+                                  _ptr(offsets), _ptr(dgu), _ptr(dy_perm), _ptr(dout), _ptr(h),
+                                  _ptr(dz_bf16), _ptr(dz), _ptr(dw_gate_up), _ptr(dw_down),
+                                  _ptr(dws_gate_up), _ptr(dws_down), _ptr(dw_router), _ptr(dbias),
+                                  _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "moe_weight_grads")
+
+
+@dataclass
+class TrainWeights:
+    """The forward weights plus the packed transposes the backward products use."""
+    fwd: LayerWeights
+    w_down_t: torch.Tensor        # E packed [F, D]
+    w_gate_up_t: torch.Tensor     # E packed [D, 2F]
+    ws_down_t: Optional[torch.Tensor]
+    ws_gate_up_t: Optional[torch.Tensor]
+    w_router_t: torch.Tensor      # packed [D, 256]
+
+
+def upload_train_weights(s: MoEShape, w_router, bias, wgu, wd, shared, device="cuda") -> TrainWeights:
+    if s.dtype != "bf16":
+        raise MoEError(MOE_ERR_UNSUPPORTED, "the training pass is bf16 only")
+    fwd = upload_weights(s, w_router, bias, wgu, wd, shared, device)
+    td = lambda a: to_device(a, s, device)
+    return TrainWeights(
+        fwd=fwd,
+        w_down_t=pack_transposed(td(wd)),
+        w_gate_up_t=pack_transposed(td(wgu)),
+        ws_down_t=None if shared is None else pack_transposed(td(shared[1])),
+        ws_gate_up_t=None if shared is None else pack_transposed(td(shared[0])),
+        w_router_t=pack_transposed(fwd.w_router, k_padded=256),
+    )
+
+
+@dataclass
+class TrainBuffers:
+    fwd: LayerBuffers
+    mask: Optional[torch.Tensor]
+    gu: torch.Tensor              # [S, 2F] + [T, 2Fs]
+    f: torch.Tensor
+    p: torch.Tensor
+    aux_loss: torch.Tensor
+    aux_coef: torch.Tensor
+    train_ws: torch.Tensor
+    dy_perm: torch.Tensor
+    dz: torch.Tensor
+    dz16: torch.Tensor
+    dh: torch.Tensor
+    dgu: torch.Tensor
+    dx_perm: torch.Tensor
+    dx_shared: Optional[torch.Tensor]
+    dx_router: torch.Tensor
+    dx: torch.Tensor
+    dw_gate_up: torch.Tensor
+    dw_down: torch.Tensor
+    dws_gate_up: Optional[torch.Tensor]
+    dws_down: Optional[torch.Tensor]
+    dw_router: torch.Tensor
+    dbias: torch.Tensor
+
+
+def alloc_train_buffers(s: MoEShape, mask: Optional[torch.Tensor] = None, device="cuda",
+                        with_x_perm: bool = False) -> TrainBuffers:
+    bf, f32 = dict(dtype=torch.bfloat16, device=device), dict(dtype=torch.float32, device=device)
+    S, T = s.S, s.T
+    c = make_shape(s)
+    return TrainBuffers(
+        fwd=alloc_buffers(s, device, with_x_perm=with_x_perm), mask=mask,
+        gu=torch.empty((S * 2 * s.F + T * 2 * s.Fs,), **bf),
+        f=torch.empty((s.E,), **f32), p=torch.empty((s.E,), **f32),
+        aux_loss=torch.empty((1,), **f32), aux_coef=torch.empty((s.E,), **f32),
+        train_ws=torch.empty((max(train_workspace_bytes(c), 256),), dtype=torch.uint8, device=device),
+        dy_perm=torch.empty((S, s.D), **bf), dz=torch.empty((T, s.E), **f32),
+        dz16=torch.empty((T, 256), **bf),
+        dh=torch.empty((S * s.F + T * s.Fs,), **bf), dgu=torch.empty((S * 2 * s.F + T * 2 * s.Fs,), **bf),
+        dx_perm=torch.empty((S, s.D), **bf),
+        dx_shared=torch.empty((T, s.D), **bf) if s.Fs else None,
+        dx_router=torch.empty((T, s.D), **bf), dx=torch.empty((T, s.D), **bf),
+        dw_gate_up=torch.empty((s.E, 2 * s.F, s.D), **bf), dw_down=torch.empty((s.E, s.D, s.F), **bf),
+        dws_gate_up=torch.empty((2 * s.Fs, s.D), **bf) if s.Fs else None,
+        dws_down=torch.empty((s.D, s.Fs), **bf) if s.Fs else None,
+        dw_router=torch.empty((s.E, s.D), **f32), dbias=torch.empty((s.E,), **f32),
+    )
+
+
+def train_forward(s: MoEShape, x: torch.Tensor, w: TrainWeights, b: TrainBuffers, beta: float,
+                  counts_global: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Masked route -> permute -> load statistics -> gate/up keeping [g | u] ->
+    down -> combine."""
+    c = make_shape(s)
+    fb, fw = b.fwd, w.fwd
+    moe_route_masked(c, x, fw.w_router, fw.bias, b.mask, fb.logits, fb.topk_idx, fb.topk_w, stream)
+    moe_permute(c, fb.topk_idx, x, fb.counts, fb.offsets, fb.sorted_token, fb.slot_of, fb.x_perm,
+                fb.workspace, stream)
+    moe_load_stats(c, fb.logits, fb.topk_idx, fb.counts, counts_global, beta, b.f, b.p, b.aux_loss,
+                   b.aux_coef, b.train_ws, stream)
+    moe_grouped_gate_up_train(c, fb.x_perm, fb.sorted_token, x, fb.offsets, fw.w_gate_up, fw.ws_gate_up,
+                              b.gu, fb.h, stream)
+    moe_grouped_down(c, fb.h, fb.offsets, fw.w_down, fw.ws_down, fb.y_perm, fb.y_shared, stream)
+    moe_combine(c, fb.y_perm, fb.y_shared, fb.slot_of, fb.topk_w, fb.out, stream)
+    return fb.out
+
+
+def train_backward(s: MoEShape, x: torch.Tensor, dout: torch.Tensor, w: TrainWeights, b: TrainBuffers,
+                   with_aux: bool = True, stream=None) -> torch.Tensor:
+    """Combine backward -> dh and SwiGLU backward -> dx -> weight gradients."""
+    c = make_shape(s)
+    fb = b.fwd
+    moe_combine_backward(c, dout, fb.y_perm, fb.slot_of, fb.topk_idx, fb.topk_w, fb.logits,
+                         b.aux_coef if with_aux else None, b.dy_perm, b.dz, b.dz16, stream)
+    moe_grouped_backward_h(c, b.dy_perm, dout, fb.offsets, w.w_down_t, w.ws_down_t, b.gu, b.dh, b.dgu,
+                           stream)
+    moe_grouped_backward_x(c, b.dgu, fb.offsets, w.w_gate_up_t, w.ws_gate_up_t, b.dz16, w.w_router_t,
+                           fb.slot_of, b.dx_perm, b.dx_shared, b.dx_router, b.dx, stream)
+    moe_weight_grads(c, x, fb.sorted_token, fb.x_perm, fb.offsets, b.dgu, b.dy_perm, dout, fb.h, b.dz16,
+                     b.dz, b.dw_gate_up, b.dw_down, b.dws_gate_up, b.dws_down, b.dw_router, b.dbias,
+                     b.train_ws, stream)
+    return b.dx

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_gemm.hip", "ffn_f32.hip", "combine.hip",
-           "pack.hip"]
+           "pack.hip", "train.hip", "wgrad.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -103,8 +103,9 @@ size_t moe_workspace_bytes(const moe_shape* shape) {
   return moe::permute_workspace_bytes(*shape);
 }
 
-int moe_route(const moe_shape* shape, const void* x, const void* w_router, const float* bias,
-              float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+int moe_route_masked(const moe_shape* shape, const void* x, const void* w_router, const float* bias,
+                     const uint8_t* mask, float* logits, int32_t* topk_idx, float* topk_w,
+                     void* stream) {
   if (int r = check_shape(shape)) return r;
   if (shape->T == 0) return ok();
   NEED_PTR(x);
@@ -116,11 +117,16 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router, const
   const moe_shape& s = *shape;
   if (s.dtype == MOE_BF16)
     return launched(moe::launch_route_bf16(s, static_cast<const moe::bf16_t*>(x),
-                                           static_cast<const moe::bf16_t*>(w_router), bias, logits,
-                                           topk_idx, topk_w, as_stream(stream)));
+                                           static_cast<const moe::bf16_t*>(w_router), bias, mask,
+                                           logits, topk_idx, topk_w, as_stream(stream)));
   return launched(moe::launch_route_f32(s, static_cast<const float*>(x),
-                                        static_cast<const float*>(w_router), bias, logits, topk_idx,
-                                        topk_w, as_stream(stream)));
+                                        static_cast<const float*>(w_router), bias, mask, logits,
+                                        topk_idx, topk_w, as_stream(stream)));
+}
+
+int moe_route(const moe_shape* shape, const void* x, const void* w_router, const float* bias,
+              float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  return moe_route_masked(shape, x, w_router, bias, nullptr, logits, topk_idx, topk_w, stream);
 }
 
 int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* counts,
@@ -333,6 +339,227 @@ int moe_combine(const moe_shape* shape, const void* y_perm, const void* y_shared
   NEED_PTR(out);
   return launched(moe::launch_combine(*shape, y_perm, y_shared, slot_of, topk_w, out,
                                       as_stream(stream)));
+}
+
+// ------------------------------------------------------------ training pass
+
+size_t moe_train_workspace_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return moe::train_workspace_bytes(*shape);
+}
+
+size_t moe_packed_transposed_bytes(int64_t count, int32_t rows, int32_t cols, int32_t k_padded) {
+  if (count < 0 || rows < 0 || cols < 0 || cols % 32 != 0 || k_padded % 16 != 0 || k_padded < rows)
+    return 0;
+  return static_cast<size_t>(count) * cols * k_padded * 2;
+}
+
+int moe_pack_weights_transposed(const void* w, void* w_packed, int64_t count, int32_t rows, int32_t cols,
+                                int32_t k_padded, void* stream) {
+  if (count < 0 || rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "negative count or size");
+  if (cols % 32 != 0 || k_padded % 16 != 0 || k_padded < rows)
+    return fail(MOE_ERR_INVALID_ARG,
+                "cols = %d must be a multiple of 32, k_padded = %d a multiple of 16 and >= rows = %d", cols,
+                k_padded, rows);
+  if (count == 0 || cols == 0 || k_padded == 0) return ok();
+  NEED_PTR(w_packed);
+  if (rows > 0) NEED_PTR(w);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(w_packed);
+  const uintptr_t in_bytes = static_cast<uintptr_t>(count) * rows * cols * 2;
+  const uintptr_t out_bytes = moe_packed_transposed_bytes(count, rows, cols, k_padded);
+  if (rows > 0 && a < b + out_bytes && b < a + in_bytes)
+    return fail(MOE_ERR_INVALID_ARG, "w and w_packed overlap");
+  return launched(moe::launch_pack_transposed(w, w_packed, count, rows, cols, k_padded, as_stream(stream)));
+}
+
+namespace {
+int check_train_shape(const moe_shape* shape) {
+  if (int r = check_shape(shape)) return r;
+  if (shape->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the training pass is bf16 only");
+  return MOE_OK;
+}
+
+int check_workspace(void* ws, size_t ws_bytes, size_t need) {
+  if (ws == nullptr || !aligned16(ws)) return fail(MOE_ERR_WORKSPACE, "workspace is NULL or not 16-byte aligned");
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_load_stats(const moe_shape* shape, const float* logits, const int32_t* topk_idx,
+                   const int32_t* counts, const int32_t* counts_global, float beta, float* f, float* p,
+                   float* aux_loss, float* aux_coef, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (!std::isfinite(beta)) return fail(MOE_ERR_INVALID_ARG, "beta is not finite");
+  NEED_PTR(counts);
+  OPT_PTR(counts_global);
+  NEED_PTR(f);
+  NEED_PTR(p);
+  NEED_PTR(aux_loss);
+  NEED_PTR(aux_coef);
+  if (shape->T > 0) {
+    NEED_PTR(logits);
+    NEED_PTR(topk_idx);
+  }
+  if (int r = check_workspace(workspace, workspace_bytes, moe::train_workspace_bytes(*shape))) return r;
+  return launched(moe::launch_load_stats(*shape, logits, topk_idx, counts, counts_global, beta, f, p,
+                                         aux_loss, aux_coef, workspace, as_stream(stream)));
+}
+
+int moe_grouped_gate_up_train(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
+                              const void* x, const int32_t* offsets, const void* w_gate_up,
+                              const void* ws_gate_up, void* gu, void* h, void* stream) {
+  if (int r = check_train_shape(shape)) return r;
+  if (shape->T == 0) return ok();
+  OPT_PTR(x_perm);
+  if (x_perm == nullptr) NEED_PTR(sorted_token);
+  NEED_PTR(x);
+  NEED_PTR(offsets);
+  NEED_PTR(w_gate_up);
+  if (shape->Fs > 0) NEED_PTR(ws_gate_up);
+  NEED_PTR(gu);
+  NEED_PTR(h);
+  const moe_shape& s = *shape;
+  using moe::bf16_t;
+  hipError_t e = moe::launch_gate_up_pre_bf16(s, static_cast<const bf16_t*>(x_perm), sorted_token,
+                                              static_cast<const bf16_t*>(x), offsets,
+                                              static_cast<const bf16_t*>(w_gate_up),
+                                              static_cast<const bf16_t*>(ws_gate_up),
+                                              static_cast<bf16_t*>(gu), as_stream(stream));
+  if (e == hipSuccess)
+    e = moe::launch_swiglu_pre(s, static_cast<const bf16_t*>(gu), offsets, static_cast<bf16_t*>(h),
+                               as_stream(stream));
+  return launched(e);
+}
+
+int moe_combine_backward(const moe_shape* shape, const void* dout, const void* y_perm,
+                         const int32_t* slot_of, const int32_t* topk_idx, const float* topk_w,
+                         const float* logits, const float* aux_coef, void* dy_perm, float* dz,
+                         void* dz_bf16, void* stream) {
+  if (int r = check_train_shape(shape)) return r;
+  if (shape->T == 0) return ok();
+  NEED_PTR(dout);
+  NEED_PTR(y_perm);
+  NEED_PTR(slot_of);
+  NEED_PTR(topk_idx);
+  NEED_PTR(topk_w);
+  NEED_PTR(logits);
+  OPT_PTR(aux_coef);
+  NEED_PTR(dy_perm);
+  NEED_PTR(dz);
+  NEED_PTR(dz_bf16);
+  using moe::bf16_t;
+  return launched(moe::launch_combine_bwd(*shape, static_cast<const bf16_t*>(dout),
+                                          static_cast<const bf16_t*>(y_perm), slot_of, topk_idx, topk_w,
+                                          logits, aux_coef, static_cast<bf16_t*>(dy_perm), dz,
+                                          static_cast<bf16_t*>(dz_bf16), as_stream(stream)));
+}
+
+int moe_grouped_backward_h(const moe_shape* shape, const void* dy_perm, const void* dout,
+                           const int32_t* offsets, const void* w_down_t, const void* ws_down_t,
+                           const void* gu, void* dh, void* dgu, void* stream) {
+  if (int r = check_train_shape(shape)) return r;
+  if (shape->T == 0) return ok();
+  NEED_PTR(dy_perm);
+  NEED_PTR(offsets);
+  NEED_PTR(w_down_t);
+  if (shape->Fs > 0) {
+    NEED_PTR(dout);
+    NEED_PTR(ws_down_t);
+  }
+  NEED_PTR(gu);
+  NEED_PTR(dh);
+  NEED_PTR(dgu);
+  const moe_shape& s = *shape;
+  using moe::bf16_t;
+  hipError_t e = moe::launch_dgrad_h_bf16(s, static_cast<const bf16_t*>(dy_perm),
+                                          static_cast<const bf16_t*>(dout), offsets,
+                                          static_cast<const bf16_t*>(w_down_t),
+                                          static_cast<const bf16_t*>(ws_down_t), static_cast<bf16_t*>(dh),
+                                          as_stream(stream));
+  if (e == hipSuccess)
+    e = moe::launch_swiglu_bwd(s, static_cast<const bf16_t*>(dh), static_cast<const bf16_t*>(gu), offsets,
+                               static_cast<bf16_t*>(dgu), as_stream(stream));
+  return launched(e);
+}
+
+int moe_grouped_backward_x(const moe_shape* shape, const void* dgu, const int32_t* offsets,
+                           const void* w_gate_up_t, const void* ws_gate_up_t, const void* dz_bf16,
+                           const void* w_router_t, const int32_t* slot_of, void* dx_perm, void* dx_shared,
+                           void* dx_router, void* dx, void* stream) {
+  if (int r = check_train_shape(shape)) return r;
+  if (shape->T == 0) return ok();
+  NEED_PTR(dgu);
+  NEED_PTR(offsets);
+  NEED_PTR(w_gate_up_t);
+  if (shape->Fs > 0) {
+    NEED_PTR(ws_gate_up_t);
+    NEED_PTR(dx_shared);
+  }
+  NEED_PTR(dz_bf16);
+  NEED_PTR(w_router_t);
+  NEED_PTR(slot_of);
+  NEED_PTR(dx_perm);
+  NEED_PTR(dx_router);
+  NEED_PTR(dx);
+  const moe_shape& s = *shape;
+  using moe::bf16_t;
+  const hipStream_t st = as_stream(stream);
+  bf16_t* dxs = s.Fs > 0 ? static_cast<bf16_t*>(dx_shared) : nullptr;
+  hipError_t e = moe::launch_dgrad_x_bf16(s, static_cast<const bf16_t*>(dgu), offsets,
+                                          static_cast<const bf16_t*>(w_gate_up_t),
+                                          static_cast<const bf16_t*>(ws_gate_up_t),
+                                          static_cast<bf16_t*>(dx_perm), dxs, st);
+  if (e == hipSuccess)
+    e = moe::launch_dense_bf16(s.T, 256, s.D, static_cast<const bf16_t*>(dz_bf16),
+                               static_cast<const bf16_t*>(w_router_t), static_cast<bf16_t*>(dx_router), st);
+  if (e == hipSuccess)
+    e = moe::launch_dx_reduce(s, static_cast<const bf16_t*>(dx_perm), dxs,
+                              static_cast<const bf16_t*>(dx_router), slot_of, static_cast<bf16_t*>(dx), st);
+  return launched(e);
+}
+
+int moe_weight_grads(const moe_shape* shape, const void* x, const int32_t* sorted_token,
+                     const void* x_perm, const int32_t* offsets, const void* dgu, const void* dy_perm,
+                     const void* dout, const void* h, const void* dz_bf16, const float* dz,
+                     void* dw_gate_up, void* dw_down, void* dws_gate_up, void* dws_down, float* dw_router,
+                     float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int r = check_train_shape(shape)) return r;
+  const moe_shape& s = *shape;
+  // with no tokens every gradient is zero and no input is read
+  if (s.T > 0) {
+    NEED_PTR(x);
+    OPT_PTR(x_perm);
+    if (x_perm == nullptr) NEED_PTR(sorted_token);
+    NEED_PTR(offsets);
+    NEED_PTR(dgu);
+    NEED_PTR(dy_perm);
+    NEED_PTR(h);
+    if (s.Fs > 0) NEED_PTR(dout);
+    if (dw_router) NEED_PTR(dz_bf16);
+    if (dbias) NEED_PTR(dz);
+  }
+  NEED_PTR(dw_gate_up);
+  NEED_PTR(dw_down);
+  if (s.Fs > 0) {
+    NEED_PTR(dws_gate_up);
+    NEED_PTR(dws_down);
+  }
+  OPT_PTR(dw_router);
+  OPT_PTR(dbias);
+  if (dbias)
+    if (int r = check_workspace(workspace, workspace_bytes, moe::train_workspace_bytes(s))) return r;
+  using moe::bf16_t;
+  const hipStream_t st = as_stream(stream);
+  hipError_t e = moe::launch_wgrad(
+      s, static_cast<const bf16_t*>(x), sorted_token, static_cast<const bf16_t*>(x_perm),
+      static_cast<const bf16_t*>(dgu), static_cast<const bf16_t*>(dy_perm), static_cast<const bf16_t*>(h),
+      static_cast<const bf16_t*>(dout), static_cast<const bf16_t*>(dz_bf16), offsets,
+      static_cast<bf16_t*>(dw_gate_up), static_cast<bf16_t*>(dw_down), static_cast<bf16_t*>(dws_gate_up),
+      static_cast<bf16_t*>(dws_down), dw_router, st);
+  if (e == hipSuccess && dbias) e = moe::launch_colsum(s, dz, dbias, workspace, st);
+  return launched(e);
 }
 
 }  // extern "C"

@@ -3,7 +3,8 @@
 // modulated by 2.5 before combining with the shared expert).  A weighted gather
 // of k expert-ordered rows per token, fp32 accumulation in slot order, one
 // rounding.  HBM-bound: one workgroup per token, 16-byte loads; the shared add
-// is fused.
+// is fused.  Slots with slot_of < 0 (a padding token, not routed) are skipped,
+// so such a token's output is the shared expert's alone.
 #include "moe_internal.h"
 
 namespace moe {
@@ -28,15 +29,30 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const bf16_t* __restr
                                                            int S, float alpha) {
   __shared__ int slot_s[kMaxK];
   __shared__ float coef_s[kMaxK];
+  __shared__ int kv_s;
   const int t = blockIdx.x;
   if (threadIdx.x < k) {
-    slot_s[threadIdx.x] = min(max(slot_of[static_cast<size_t>(t) * k + threadIdx.x], 0), S - 1);
+    slot_s[threadIdx.x] = slot_of[static_cast<size_t>(t) * k + threadIdx.x];
     coef_s[threadIdx.x] = alpha * topk_w[static_cast<size_t>(t) * k + threadIdx.x];
   }
   __syncthreads();
+  if (threadIdx.x == 0) {
+    // keep the routed slots, in slot order
+    int kv = 0;
+    for (int j = 0; j < k; ++j) {
+      const int p = slot_s[j];
+      if (p < 0) continue;
+      slot_s[kv] = min(p, S - 1);
+      coef_s[kv] = coef_s[j];
+      ++kv;
+    }
+    kv_s = kv;
+  }
+  __syncthreads();
+  const int kv = kv_s;
   for (int c = threadIdx.x * 8; c < D; c += blockDim.x * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
+    for (int j = 0; j < kv; ++j) {
       float v[8];
       load8(y_perm + static_cast<size_t>(slot_s[j]) * D + c, v);
       const float cj = coef_s[j];
@@ -64,15 +80,30 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
                                                           int S, float alpha) {
   __shared__ int slot_s[kMaxK];
   __shared__ float coef_s[kMaxK];
+  __shared__ int kv_s;
   const int t = blockIdx.x;
   if (threadIdx.x < k) {
-    slot_s[threadIdx.x] = min(max(slot_of[static_cast<size_t>(t) * k + threadIdx.x], 0), S - 1);
+    slot_s[threadIdx.x] = slot_of[static_cast<size_t>(t) * k + threadIdx.x];
     coef_s[threadIdx.x] = alpha * topk_w[static_cast<size_t>(t) * k + threadIdx.x];
   }
   __syncthreads();
+  if (threadIdx.x == 0) {
+    // keep the routed slots, in slot order
+    int kv = 0;
+    for (int j = 0; j < k; ++j) {
+      const int p = slot_s[j];
+      if (p < 0) continue;
+      slot_s[kv] = min(p, S - 1);
+      coef_s[kv] = coef_s[j];
+      ++kv;
+    }
+    kv_s = kv;
+  }
+  __syncthreads();
+  const int kv = kv_s;
   for (int c = threadIdx.x * 4; c < D; c += blockDim.x * 4) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
+    for (int j = 0; j < kv; ++j) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(y_perm + static_cast<size_t>(slot_s[j]) * D + c);
       const float cj = coef_s[j];
 #pragma unroll

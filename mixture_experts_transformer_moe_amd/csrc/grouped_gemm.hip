@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       __syncthreads();
     }
     if (tid == 0) {
-      const int routed_total = tile_end[E - 1];
+      const int routed_total = E > 0 ? tile_end[E - 1] : 0;
       // Shared-expert row-block height: the tiles run in rounds of G (one per
       // workgroup), routed tiles first, so the shared tiles fill the last
       // rounds.  Take the fewest rounds, and for that count the shortest
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       }
       shared_bm = best_bm;
       tile_end[E] = routed_total + (g.has_shared ? (g.T + best_bm - 1) / best_bm * nt_s : 0);
-      row_base[E] = min(max(g.offsets[E], row_base[E - 1]), g.S);
+      row_base[E] = E > 0 ? min(max(g.offsets[E], row_base[E - 1]), g.S) : 0;
     }
     __syncthreads();
   }
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     // out of the tile loop it would hold registers across the whole stream
     int lane = tid & 63;
     asm volatile("" : "+v"(lane));
-    if (MODE == kGateUp) {
+    if (MODE == kGateUp && E > 0) {
       // gate_up: the shared expert's tiles (weights L2-resident after the
       // first few) are spread evenly through the schedule instead of filling
       // the last round, so that every round keeps most CUs on the HBM weight
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
             float y[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              if (MODE == kGateUp) {
+              if (MODE == kGateUp && E > 0) {
                 float gv = acc[m][j][4 * q + e], uv = acc[m][j + NB / 2][4 * q + e];
                 if constexpr (W8) {
                   gv *= wsc[j][4 * q + e];
@@ -401,11 +401,10 @@ int persistent_grid() {
 // MFMAs) measured best among the shapes whose accumulators and weight ring fit
 // the registers, when the output width allows their wider tiles.
 template <int MODE, bool W8>
-hipError_t launch_tiles(const GemmArgs& a, const moe_shape& s, hipStream_t st) {
+hipError_t launch_tiles(const GemmArgs& a, int mean_rows, hipStream_t st) {
   // the weight ring's depth: 16 K steps of bf16 weights, 8 ring steps (16 K
   // steps) of FP8 ones
   constexpr int P = W8 ? 8 : 16;
-  const int mean_rows = (s.T * s.k) / s.E;
   const int wide = MODE == kGateUp ? 256 : 512;            // output columns of an NB = 4 tile
   if (mean_rows >= 192 && a.N % wide == 0 && (!a.has_shared || a.Ns % wide == 0))
     grouped_gemm_kernel<MODE, 96, 4, 8, W8><<<persistent_grid(), kThreads, 0, st>>>(a);
@@ -419,6 +418,8 @@ hipError_t launch_tiles(const GemmArgs& a, const moe_shape& s, hipStream_t st) {
     grouped_gemm_kernel<MODE, 32, 2, P, W8><<<persistent_grid(), kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
+
+int mean_rows(const moe_shape& s) { return (s.T * s.k) / s.E; }
 
 GemmArgs gate_up_args(const moe_shape& s, const bf16_t* x_perm, const int32_t* sorted_token,
                       const bf16_t* x, const int32_t* offsets, bf16_t* h) {
@@ -462,6 +463,89 @@ GemmArgs down_args(const moe_shape& s, const bf16_t* h, const int32_t* offsets, 
 
 }  // namespace
 
+// ---- training pass: the same kernel in its plain mode (no SwiGLU) on other
+// operands.  Packed transposed weights (moe_pack_weights_transposed) turn the
+// backward products into the forward's form: rows of the packed matrix are
+// output columns, its K the reduction.
+
+hipError_t launch_gate_up_pre_bf16(const moe_shape& s, const bf16_t* x_perm,
+                                   const int32_t* sorted_token, const bf16_t* x,
+                                   const int32_t* offsets, const bf16_t* wgu, const bf16_t* wsgu,
+                                   bf16_t* gu, hipStream_t st) {
+  // [g | u] = a [W_g; W_u]^T: the gate/up matrix read as one [2F, D] matrix
+  GemmArgs a = gate_up_args(s, x_perm, sorted_token, x, offsets, gu);
+  a.out_shared = gu + static_cast<size_t>(s.T) * s.k * 2 * s.F;
+  a.N = 2 * s.F;
+  a.Ns = 2 * s.Fs;
+  a.w_routed = reinterpret_cast<const unsigned char*>(wgu);
+  a.w_shared = reinterpret_cast<const unsigned char*>(wsgu);
+  return launch_tiles<kDown, false>(a, mean_rows(s), st);
+}
+
+hipError_t launch_dgrad_h_bf16(const moe_shape& s, const bf16_t* dy_perm, const bf16_t* dout,
+                               const int32_t* offsets, const bf16_t* wd_t, const bf16_t* wsd_t,
+                               bf16_t* dh, hipStream_t st) {
+  // dh = dy W_d: rows of W_d^T [F, D] are the outputs, D the reduction; the
+  // shared expert's output gradient is dout itself
+  GemmArgs a{};
+  a.a_routed = dy_perm;
+  a.a_shared = dout;
+  a.out_routed = dh;
+  a.out_shared = dh + static_cast<size_t>(s.T) * s.k * s.F;
+  a.offsets = offsets;
+  a.T = s.T;
+  a.E = s.E;
+  a.S = s.T * s.k;
+  a.K = s.D;
+  a.Ks = s.D;
+  a.N = s.F;
+  a.Ns = s.Fs;
+  a.has_shared = s.Fs > 0;
+  a.w_routed = reinterpret_cast<const unsigned char*>(wd_t);
+  a.w_shared = reinterpret_cast<const unsigned char*>(wsd_t);
+  return launch_tiles<kDown, false>(a, mean_rows(s), st);
+}
+
+hipError_t launch_dgrad_x_bf16(const moe_shape& s, const bf16_t* dgu, const int32_t* offsets,
+                               const bf16_t* wgu_t, const bf16_t* wsgu_t, bf16_t* dx_perm,
+                               bf16_t* dx_shared, hipStream_t st) {
+  // da = [dg | du] [W_g; W_u]: rows of the transposed gate/up matrix [D, 2F]
+  GemmArgs a{};
+  a.a_routed = dgu;
+  a.a_shared = dgu + static_cast<size_t>(s.T) * s.k * 2 * s.F;
+  a.out_routed = dx_perm;
+  a.out_shared = dx_shared;
+  a.offsets = offsets;
+  a.T = s.T;
+  a.E = s.E;
+  a.S = s.T * s.k;
+  a.K = 2 * s.F;
+  a.Ks = 2 * s.Fs;
+  a.N = s.D;
+  a.Ns = s.D;
+  a.has_shared = s.Fs > 0;
+  a.w_routed = reinterpret_cast<const unsigned char*>(wgu_t);
+  a.w_shared = reinterpret_cast<const unsigned char*>(wsgu_t);
+  return launch_tiles<kDown, false>(a, mean_rows(s), st);
+}
+
+hipError_t launch_dense_bf16(int rows, int K, int N, const bf16_t* a_rows, const bf16_t* w_packed,
+                             bf16_t* out, hipStream_t st) {
+  // out [rows, N] = a [rows, K] W^T with W packed [N, K]: the shared group
+  // alone, no routed groups
+  GemmArgs a{};
+  a.a_shared = a_rows;
+  a.w_shared = reinterpret_cast<const unsigned char*>(w_packed);
+  a.out_shared = out;
+  a.T = rows;
+  a.E = 0;
+  a.S = 0;
+  a.Ks = K;
+  a.Ns = N;
+  a.has_shared = 1;
+  return launch_tiles<kDown, false>(a, rows, st);
+}
+
 hipError_t launch_gate_up_bf16(const moe_shape& s, const bf16_t* x_perm,
                                const int32_t* sorted_token, const bf16_t* x,
                                const int32_t* offsets, const bf16_t* wgu, const bf16_t* wsgu,
@@ -469,7 +553,7 @@ hipError_t launch_gate_up_bf16(const moe_shape& s, const bf16_t* x_perm,
   GemmArgs a = gate_up_args(s, x_perm, sorted_token, x, offsets, h);
   a.w_routed = reinterpret_cast<const unsigned char*>(wgu);
   a.w_shared = reinterpret_cast<const unsigned char*>(wsgu);
-  return launch_tiles<kGateUp, false>(a, s, st);
+  return launch_tiles<kGateUp, false>(a, mean_rows(s), st);
 }
 
 hipError_t launch_down_bf16(const moe_shape& s, const bf16_t* h, const int32_t* offsets,
@@ -478,7 +562,7 @@ hipError_t launch_down_bf16(const moe_shape& s, const bf16_t* h, const int32_t* 
   GemmArgs a = down_args(s, h, offsets, y_perm, y_shared);
   a.w_routed = reinterpret_cast<const unsigned char*>(wd);
   a.w_shared = reinterpret_cast<const unsigned char*>(wsd);
-  return launch_tiles<kDown, false>(a, s, st);
+  return launch_tiles<kDown, false>(a, mean_rows(s), st);
 }
 
 hipError_t launch_gate_up_fp8(const moe_shape& s, const bf16_t* x_perm, const int32_t* sorted_token,
@@ -490,7 +574,7 @@ hipError_t launch_gate_up_fp8(const moe_shape& s, const bf16_t* x_perm, const in
   a.w_shared = wsgu;
   a.s_routed = sgu;
   a.s_shared = ssgu;
-  return launch_tiles<kGateUp, true>(a, s, st);
+  return launch_tiles<kGateUp, true>(a, mean_rows(s), st);
 }
 
 hipError_t launch_down_fp8(const moe_shape& s, const bf16_t* h, const int32_t* offsets,
@@ -501,7 +585,7 @@ hipError_t launch_down_fp8(const moe_shape& s, const bf16_t* h, const int32_t* o
   a.w_shared = wsd;
   a.s_routed = sd;
   a.s_shared = ssd;
-  return launch_tiles<kDown, true>(a, s, st);
+  return launch_tiles<kDown, true>(a, mean_rows(s), st);
 }
 
 }  // namespace moe

@@ -36,12 +36,13 @@ __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-
 
 // --------------------------------------------------------------- launchers
 // All return hipSuccess or the launch error; they assume validated arguments.
+// mask: null, or one byte per token (0 = padding: not routed, expert -1)
 hipError_t launch_route_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* wr,
-                             const float* bias, float* logits, int32_t* idx, float* w,
-                             hipStream_t st);
+                             const float* bias, const uint8_t* mask, float* logits, int32_t* idx,
+                             float* w, hipStream_t st);
 hipError_t launch_route_f32(const moe_shape& s, const float* x, const float* wr,
-                            const float* bias, float* logits, int32_t* idx, float* w,
-                            hipStream_t st);
+                            const float* bias, const uint8_t* mask, float* logits, int32_t* idx,
+                            float* w, hipStream_t st);
 
 size_t permute_workspace_bytes(const moe_shape& s);
 hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x, int32_t* counts,
@@ -55,6 +56,21 @@ hipError_t launch_gate_up_bf16(const moe_shape& s, const bf16_t* x_perm,
 hipError_t launch_down_bf16(const moe_shape& s, const bf16_t* h, const int32_t* offsets,
                             const bf16_t* wd, const bf16_t* wsd, bf16_t* y_perm,
                             bf16_t* y_shared, hipStream_t st);
+// training pass (grouped_gemm.hip): pre-activations [g | u] of every routed
+// row and of the shared expert; dh = dy W_d; da = [dg | du] [W_g; W_u]; a
+// dense product out = a W^T with W packed [N, K]
+hipError_t launch_gate_up_pre_bf16(const moe_shape& s, const bf16_t* x_perm,
+                                   const int32_t* sorted_token, const bf16_t* x,
+                                   const int32_t* offsets, const bf16_t* wgu, const bf16_t* wsgu,
+                                   bf16_t* gu, hipStream_t st);
+hipError_t launch_dgrad_h_bf16(const moe_shape& s, const bf16_t* dy_perm, const bf16_t* dout,
+                               const int32_t* offsets, const bf16_t* wd_t, const bf16_t* wsd_t,
+                               bf16_t* dh, hipStream_t st);
+hipError_t launch_dgrad_x_bf16(const moe_shape& s, const bf16_t* dgu, const int32_t* offsets,
+                               const bf16_t* wgu_t, const bf16_t* wsgu_t, bf16_t* dx_perm,
+                               bf16_t* dx_shared, hipStream_t st);
+hipError_t launch_dense_bf16(int rows, int K, int N, const bf16_t* a_rows, const bf16_t* w_packed,
+                             bf16_t* out, hipStream_t st);
 hipError_t launch_gate_up_f32(const moe_shape& s, const float* x_perm,
                               const int32_t* sorted_token, const float* x,
                               const int32_t* offsets, const float* wgu, const float* wsgu,
@@ -90,5 +106,28 @@ hipError_t launch_pack(const void* src, void* dst, int64_t count, int rows, int 
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_shared,
                           const int32_t* slot_of, const float* topk_w, void* out,
                           hipStream_t st);
+
+// ---------------------------------------------------------- training pass
+hipError_t launch_pack_transposed(const void* src, void* dst, int64_t count, int rows, int cols, int kp,
+                                  hipStream_t st);
+size_t train_workspace_bytes(const moe_shape& s);
+hipError_t launch_swiglu_pre(const moe_shape& s, const bf16_t* gu, const int32_t* offsets, bf16_t* h,
+                             hipStream_t st);
+hipError_t launch_swiglu_bwd(const moe_shape& s, const bf16_t* dh, const bf16_t* gu,
+                             const int32_t* offsets, bf16_t* dgu, hipStream_t st);
+hipError_t launch_combine_bwd(const moe_shape& s, const bf16_t* dout, const bf16_t* y_perm,
+                              const int32_t* slot_of, const int32_t* topk_idx, const float* topk_w,
+                              const float* logits, const float* coef, bf16_t* dy_perm, float* dz,
+                              bf16_t* dz16, hipStream_t st);
+hipError_t launch_dx_reduce(const moe_shape& s, const bf16_t* dx_perm, const bf16_t* dx_shared,
+                            const bf16_t* dx_router, const int32_t* slot_of, bf16_t* dx, hipStream_t st);
+hipError_t launch_load_stats(const moe_shape& s, const float* logits, const int32_t* topk_idx,
+                             const int32_t* counts, const int32_t* counts_global, float beta, float* f,
+                             float* p, float* loss, float* coef, void* ws, hipStream_t st);
+hipError_t launch_colsum(const moe_shape& s, const float* m, float* out, void* ws, hipStream_t st);
+hipError_t launch_wgrad(const moe_shape& s, const bf16_t* x, const int32_t* sorted_token,
+                        const bf16_t* x_perm, const bf16_t* dgu, const bf16_t* dy, const bf16_t* h,
+                        const bf16_t* dout, const bf16_t* dz16, const int32_t* offsets, bf16_t* dwgu,
+                        bf16_t* dwd, bf16_t* dwsgu, bf16_t* dwsd, float* dwr, hipStream_t st);
 
 }  // namespace moe

@@ -35,6 +35,36 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, T*
   }
 }
 
+// Transposed packing for the backward products: matrix i of src [count, rows,
+// cols] becomes its transpose [cols, kp] in the packed order above, with
+// columns k >= rows of the transpose zero (kp >= rows, kp % 16 == 0).  Lanes
+// of a wave read consecutive source columns of the same source row.
+__global__ __launch_bounds__(256) void pack_transposed_kernel(const uint16_t* __restrict__ src,
+                                                              uint16_t* __restrict__ dst,
+                                                              int64_t count, int rows, int cols,
+                                                              int kp) {
+  const int cb = kp >> 4;                                            // column blocks of the transpose
+  const int64_t per_mat = static_cast<int64_t>(cols) * kp / 8;       // 8-element groups
+  const int64_t groups = count * per_mat;
+  for (int64_t gi = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; gi < groups;
+       gi += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t mi = gi / per_mat;
+    const int64_t in = gi - mi * per_mat;
+    const int64_t blk = in >> 6;
+    const int lane = static_cast<int>(in & 63);
+    const int nb = static_cast<int>(blk / cb), kb = static_cast<int>(blk % cb);
+    const int trow = nb * 32 + (lane & 31);                          // a source column
+    const int tcol = kb * 16 + 8 * (lane >> 5);                      // source rows tcol..tcol+7
+    const uint16_t* s = src + mi * rows * static_cast<int64_t>(cols) + trow;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tcol + e < rows ? s[static_cast<int64_t>(tcol + e) * cols] : 0;
+    uint16_t* d = dst + gi * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = v[e];
+  }
+}
+
 // E4M3 code of a finite fp32 value: round to nearest, ties to even, magnitudes
 // past 448 saturating to 448 (OCP FP8 E4M3: bias 7, subnormals below 2^-6, no
 // infinities, 0x7F / 0xFF are NaN and never produced).
@@ -124,6 +154,17 @@ hipError_t launch_pack(const void* src, void* dst, int64_t count, int rows, int 
   else
     pack_kernel<float><<<blocks, 256, 0, st>>>(static_cast<const float*>(src), static_cast<float*>(dst),
                                                count, rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_transposed(const void* src, void* dst, int64_t count, int rows, int cols, int kp,
+                                  hipStream_t st) {
+  const int64_t groups = count * static_cast<int64_t>(cols) * kp / 8;
+  if (groups == 0) return hipSuccess;
+  const int64_t want = (groups + 255) / 256;
+  const int blocks = static_cast<int>(want < 65536 ? want : 65536);
+  pack_transposed_kernel<<<blocks, 256, 0, st>>>(static_cast<const uint16_t*>(src),
+                                                 static_cast<uint16_t*>(dst), count, rows, cols, kp);
   return hipGetLastError();
 }
 

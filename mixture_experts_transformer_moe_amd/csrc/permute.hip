@@ -15,6 +15,9 @@
 //           expert's tokens end up in ascending token order
 //   gather  x_perm[p] = x[sorted_token[p]] with 16-byte loads and stores,
 //           flattened over all (row, chunk) pairs
+// A negative expert index marks a slot that is not routed (a padding token):
+// it takes no position, its slot_of is -1, and offsets[E] is the number of
+// routed slots.
 #include "moe_internal.h"
 
 namespace moe {
@@ -24,7 +27,7 @@ constexpr int kTB = 256;        // tokens per block
 constexpr int kMaxE = 256;
 static_assert(kTB == kMaxE, "the scatter kernel keeps one thread per expert");
 
-__device__ __forceinline__ int clamp_e(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+__device__ __forceinline__ int clamp_e(int e, int E) { return e >= E ? E - 1 : e; }
 
 __global__ __launch_bounds__(kTB) void perm_hist_kernel(const int32_t* __restrict__ idx, int T,
                                                         int E, int k, int32_t* __restrict__ blk) {
@@ -33,7 +36,10 @@ __global__ __launch_bounds__(kTB) void perm_hist_kernel(const int32_t* __restric
   __syncthreads();
   const int t = blockIdx.x * kTB + threadIdx.x;
   if (t < T)
-    for (int j = 0; j < k; ++j) atomicAdd(&hist[clamp_e(idx[static_cast<size_t>(t) * k + j], E)], 1);
+    for (int j = 0; j < k; ++j) {
+      const int e = clamp_e(idx[static_cast<size_t>(t) * k + j], E);
+      if (e >= 0) atomicAdd(&hist[e], 1);
+    }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kTB) blk[static_cast<size_t>(blockIdx.x) * E + e] = hist[e];
 }
@@ -42,7 +48,7 @@ __global__ __launch_bounds__(kTB) void perm_hist_kernel(const int32_t* __restric
 // in the blocks before this one, then an exclusive scan of the totals over
 // the experts in LDS.
 __global__ __launch_bounds__(kTB) void perm_scatter_kernel(const int32_t* __restrict__ idx, int T,
-                                                           int E, int k, int nb, int S,
+                                                           int E, int k, int nb,
                                                            const int32_t* __restrict__ blk,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets,
@@ -83,12 +89,10 @@ __global__ __launch_bounds__(kTB) void perm_scatter_kernel(const int32_t* __rest
   }
   const int excl = scan[e] - total;
   base[e] = excl + before;
-  if (blockIdx.x == 0) {
-    if (e < E) {
-      counts[e] = total;
-      offsets[e] = excl;
-    }
-    if (e == 0) offsets[E] = S;
+  if (blockIdx.x == 0 && e < E) {
+    counts[e] = total;
+    offsets[e] = excl;
+    if (e == E - 1) offsets[E] = scan[e];
   }
   __syncthreads();
   const int local = threadIdx.x;
@@ -96,12 +100,18 @@ __global__ __launch_bounds__(kTB) void perm_scatter_kernel(const int32_t* __rest
   const int word = local >> 5;
   const uint32_t bit = 1u << (local & 31);
   if (t < T)
-    for (int j = 0; j < k; ++j)
-      atomicOr(&chose[clamp_e(idx[static_cast<size_t>(t) * k + j], E)][word], bit);
+    for (int j = 0; j < k; ++j) {
+      const int ej = clamp_e(idx[static_cast<size_t>(t) * k + j], E);
+      if (ej >= 0) atomicOr(&chose[ej][word], bit);
+    }
   __syncthreads();
   if (t < T) {
     for (int j = 0; j < k; ++j) {
       const int ej = clamp_e(idx[static_cast<size_t>(t) * k + j], E);
+      if (ej < 0) {
+        slot_of[static_cast<size_t>(t) * k + j] = -1;
+        continue;
+      }
       int rank = __popc(chose[ej][word] & (bit - 1u));
       for (int w = 0; w < word; ++w) rank += __popc(chose[ej][w]);
       const int pos = base[ej] + rank;
@@ -115,7 +125,7 @@ __global__ __launch_bounds__(kTB) void perm_scatter_kernel(const int32_t* __rest
 // decode-sized): the histogram, the scan over the experts and the scatter,
 // without the workspace round trip and the second launch.
 __global__ __launch_bounds__(kTB) void perm_single_block_kernel(const int32_t* __restrict__ idx, int T,
-                                                                int E, int k, int S,
+                                                                int E, int k,
                                                                 int32_t* __restrict__ counts,
                                                                 int32_t* __restrict__ offsets,
                                                                 int32_t* __restrict__ sorted_token,
@@ -132,6 +142,7 @@ __global__ __launch_bounds__(kTB) void perm_single_block_kernel(const int32_t* _
   if (t < T)
     for (int j = 0; j < k; ++j) {
       const int e = clamp_e(idx[static_cast<size_t>(t) * k + j], E);
+      if (e < 0) continue;
       atomicAdd(&hist[e], 1);
       atomicOr(&chose[e][word], bit);
     }
@@ -148,11 +159,15 @@ __global__ __launch_bounds__(kTB) void perm_single_block_kernel(const int32_t* _
   if (t < E) {
     counts[t] = total;
     offsets[t] = scan[t] - total;
+    if (t == E - 1) offsets[E] = scan[t];
   }
-  if (t == 0) offsets[E] = S;
   if (t < T) {
     for (int j = 0; j < k; ++j) {
       const int e = clamp_e(idx[static_cast<size_t>(t) * k + j], E);
+      if (e < 0) {
+        slot_of[static_cast<size_t>(t) * k + j] = -1;
+        continue;
+      }
       int rank = __popc(chose[e][word] & (bit - 1u));
       for (int w = 0; w < word; ++w) rank += __popc(chose[e][w]);
       const int pos = scan[e] - hist[e] + rank;
@@ -206,12 +221,12 @@ hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x,
   const int S = s.T * s.k;
   hipError_t err;
   if (nb == 1) {
-    perm_single_block_kernel<<<1, kTB, 0, st>>>(idx, s.T, s.E, s.k, S, counts, offsets,
+    perm_single_block_kernel<<<1, kTB, 0, st>>>(idx, s.T, s.E, s.k, counts, offsets,
                                                 sorted_token, slot_of);
   } else {
     perm_hist_kernel<<<nb, kTB, 0, st>>>(idx, s.T, s.E, s.k, blk);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    perm_scatter_kernel<<<nb, kTB, 0, st>>>(idx, s.T, s.E, s.k, nb, S, blk, counts, offsets,
+    perm_scatter_kernel<<<nb, kTB, 0, st>>>(idx, s.T, s.E, s.k, nb, blk, counts, offsets,
                                             sorted_token, slot_of);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;

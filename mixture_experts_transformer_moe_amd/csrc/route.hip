@@ -56,8 +56,10 @@ __device__ __forceinline__ float row_sum_f32(float v) {
 constexpr int kTopkThreads = 256;              // 4 waves x 4 tokens
 constexpr int kTopkTokens = kTopkThreads / 16;
 
-// Top-k of the stored logits, 16 lanes per token (E <= 256, k <= 16).
+// Top-k of the stored logits, 16 lanes per token (E <= 256, k <= 16).  A
+// token whose mask byte is 0 (padding) is not routed: expert -1, weight 0.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ logits,
+                                                            const uint8_t* __restrict__ mask,
                                                             int32_t* __restrict__ idx,
                                                             float* __restrict__ wout, int T, int E, int k) {
   const int c = threadIdx.x & 15;
@@ -95,9 +97,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   // sigmoid of the selected logits (exact fp32 values), renormalised
   const float s = c < k ? 1.0f / (1.0f + expf(-z[my_e])) : 0.f;
   const float sum = row_sum_f32(s);
+  const bool routed = mask == nullptr || mask[t] != 0;
   if (t_raw < T && c < k) {
-    idx[static_cast<size_t>(t) * k + c] = my_e;
-    wout[static_cast<size_t>(t) * k + c] = s / sum;
+    idx[static_cast<size_t>(t) * k + c] = routed ? my_e : -1;
+    wout[static_cast<size_t>(t) * k + c] = routed ? s / sum : 0.f;
   }
 }
 
@@ -246,15 +249,16 @@ __global__ __launch_bounds__(64) void route_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_topk(const moe_shape& s, const float* logits, int32_t* idx, float* w, hipStream_t st) {
+hipError_t launch_topk(const moe_shape& s, const float* logits, const uint8_t* mask, int32_t* idx,
+                       float* w, hipStream_t st) {
   const int blocks = (s.T + kTopkTokens - 1) / kTopkTokens;
-  topk_kernel<<<blocks, kTopkThreads, 0, st>>>(logits, idx, w, s.T, s.E, s.k);
+  topk_kernel<<<blocks, kTopkThreads, 0, st>>>(logits, mask, idx, w, s.T, s.E, s.k);
   return hipGetLastError();
 }
 
 hipError_t launch_route_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* wr,
-                             const float* bias, float* logits, int32_t* idx, float* w,
-                             hipStream_t st) {
+                             const float* bias, const uint8_t* mask, float* logits, int32_t* idx,
+                             float* w, hipStream_t st) {
   // 64 x 64 blocks when they are enough to fill the chip, else 32 x 32 blocks
   // with the K split over the workgroup's waves
   const int big = ((s.T + 63) / 64) * ((s.E + 63) / 64);
@@ -265,15 +269,15 @@ hipError_t launch_route_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* 
     route_bf16_kernel<32, 32, 4, 4><<<blocks, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
   }
   if (hipError_t e = hipGetLastError()) return e;
-  return launch_topk(s, logits, idx, w, st);
+  return launch_topk(s, logits, mask, idx, w, st);
 }
 
 hipError_t launch_route_f32(const moe_shape& s, const float* x, const float* wr,
-                            const float* bias, float* logits, int32_t* idx, float* w,
-                            hipStream_t st) {
+                            const float* bias, const uint8_t* mask, float* logits, int32_t* idx,
+                            float* w, hipStream_t st) {
   route_f32_kernel<<<s.T, 64, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
   if (hipError_t e = hipGetLastError()) return e;
-  return launch_topk(s, logits, idx, w, st);
+  return launch_topk(s, logits, mask, idx, w, st);
 }
 
 }  // namespace moe

@@ -148,3 +148,37 @@ def test_fp8_sizes_and_argument_checks(L):
     assert L.moe_grouped_down_fp8(ctypes.byref(sb), *([ctypes.c_void_p(1 << 20)] * 3), None,
                                   *([ctypes.c_void_p(1 << 20)] * 4), None) == binding.MOE_ERR_INVALID_ARG
     assert b"w_down_scale" in L.moe_last_error()
+
+
+def test_training_entry_points_check_arguments(L):
+    s32 = binding.make_shape(configs.TINY_F32)
+    s16 = binding.make_shape(configs.variant(configs.XS2_T4096, T=64))
+    p = ctypes.c_void_p(1 << 20)
+    assert L.moe_train_workspace_bytes(ctypes.byref(s16)) >= 256
+    # transposed packing: the transpose's rows (source columns) in 32s, k_padded >= rows in 16s
+    assert L.moe_packed_transposed_bytes(4, 2048, 512, 2048) == 4 * 512 * 2048 * 2
+    assert L.moe_packed_transposed_bytes(1, 16, 2048, 256) == 2048 * 256 * 2
+    for bad in ((1, 32, 48, 32), (1, 40, 64, 32), (1, 32, 64, 40), (-1, 32, 64, 32)):
+        assert L.moe_packed_transposed_bytes(*bad) == 0
+    assert L.moe_pack_weights_transposed(p, ctypes.c_void_p(1 << 30), 1, 40, 64, 32, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights_transposed(p, ctypes.c_void_p((1 << 20) + 64), 1, 32, 64, 32, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    assert b"overlap" in L.moe_last_error()
+    # the training pass is bf16 only
+    args = [p] * 11
+    assert L.moe_combine_backward(ctypes.byref(s32), *args) == binding.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_gate_up_train(ctypes.byref(s32), *([p] * 9)) == binding.MOE_ERR_UNSUPPORTED
+    # missing pointers and workspace are caught before any launch
+    assert L.moe_combine_backward(ctypes.byref(s16), None, *([p] * 10)) == binding.MOE_ERR_INVALID_ARG
+    assert b"dout" in L.moe_last_error()
+    assert L.moe_load_stats(ctypes.byref(s16), p, p, p, None, ctypes.c_float(0.1), p, p, p, p, None, 0,
+                            None) == binding.MOE_ERR_WORKSPACE
+    assert L.moe_load_stats(ctypes.byref(s16), p, p, p, None, ctypes.c_float(float("nan")), p, p, p, p, p,
+                            1 << 20, None) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_backward_x(ctypes.byref(s16), *([p] * 6), None, *([p] * 5)) == \
+        binding.MOE_ERR_INVALID_ARG
+    assert b"slot_of" in L.moe_last_error()
+    wg = [p] * 16
+    wg[14] = p   # dbias requested: needs the workspace
+    assert L.moe_weight_grads(ctypes.byref(s16), *wg, None, 0, None) == binding.MOE_ERR_WORKSPACE

@@ -1,0 +1,212 @@
+"""GPU parity of the training pass (padding mask, load statistics, auxiliary
+loss, backward) against the CPU oracle (oracle/train_oracle.py), through the C
+ABI.
+
+Routing, counts and expert order bit-exact (decided on the GPU's fp32
+logits); bf16 tensors within 2e-2 * max|oracle| of the tensor (one bf16
+rounding of stored intermediates, fp32 accumulation); the load statistics,
+which the GPU sums in fp32 from its fp32 logits, within 1e-5 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from oracle import train_oracle as TR
+from mixture_experts_transformer_moe_amd import binding, configs
+from mixture_experts_transformer_moe_amd.inputs import LayerInputs, dout_encoded, token_mask
+from tests.gpu_common import StackedInputs, assert_close_rel, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+SMALL = configs.variant(configs.XS2_T4096, name="train_small_t300", T=300, D=256, E=16, k=4, F=256,
+                        Fs=256, pad_frac=0.1, seq_len=64, aux_coef=0.5)
+
+
+def run_train(s, inp, mask, dout_bits, beta, counts_global=None, gather=True):
+    say(f"train {s.name} T={s.T} D={s.D} E={s.E} k={s.k} F={s.F} Fs={s.Fs} beta={beta} "
+        f"padding={int((mask == 0).sum())} gather={gather}")
+    w = binding.upload_train_weights(s, inp.w_router, inp.bias, inp.wgu, inp.wd, inp.shared())
+    x = binding.to_device(inp.x, s, "cuda")
+    m = torch.from_numpy(mask).cuda()
+    dout = binding.to_device(dout_bits, s, "cuda")
+    b = binding.alloc_train_buffers(s, m, with_x_perm=not gather)
+    cg = None if counts_global is None else torch.from_numpy(np.asarray(counts_global, np.int32)).cuda()
+    binding.train_forward(s, x, w, b, beta, cg)
+    binding.train_backward(s, x, dout, w, b, with_aux=beta != 0)
+    torch.cuda.synchronize()
+    say("train pass done")
+    return w, b
+
+
+def routing_of(s, b, mask):
+    """Oracle routing on the GPU's fp32 logits, checked bit-exact."""
+    fb = b.fwd
+    r = TR.route_masked(fb.logits.cpu().numpy().astype(np.float64), s.k, mask)
+    assert np.array_equal(fb.topk_idx.cpu().numpy(), r.topk_idx), "topk_idx differs"
+    assert np.array_equal(fb.counts.cpu().numpy(), r.counts), "counts differ"
+    assert np.array_equal(fb.offsets.cpu().numpy(), r.offsets), "offsets differ"
+    n = int(r.offsets[-1])
+    assert np.array_equal(fb.sorted_token.cpu().numpy()[:n], r.sorted_token), "sorted_token differs"
+    assert np.array_equal(fb.slot_of.cpu().numpy(), r.slot_of), "slot_of differs"
+    np.testing.assert_allclose(fb.topk_w.cpu().numpy(), r.topk_w, rtol=1e-6, atol=0)
+    return r
+
+
+def check_stats(s, b, r, beta, counts_global=None):
+    f, p, N = TR.load_stats(r, counts_global)
+    np.testing.assert_allclose(b.f.cpu().numpy(), f, rtol=1e-6, atol=1e-9)
+    np.testing.assert_allclose(b.p.cpu().numpy(), p, rtol=1e-5, atol=1e-7)
+    loss = TR.aux_loss(r, beta, counts_global)
+    assert abs(float(b.aux_loss.cpu()[0]) - loss) <= 1e-5 * max(abs(loss), 1e-12), (float(b.aux_loss.cpu()[0]), loss)
+    coef = TR.aux_coefficients(r, beta, counts_global)
+    if coef is not None:
+        np.testing.assert_allclose(b.aux_coef.cpu().numpy(), coef, rtol=1e-5, atol=1e-12)
+    say(f"stats: N={N} loss={loss:.6e}")
+
+
+def full_parity(s, mask=None, beta=None, counts_global=None, gather=True):
+    inp = StackedInputs(LayerInputs(s))
+    mask = token_mask(s) if mask is None else mask
+    beta = s.aux_coef if beta is None else beta
+    dout = dout_encoded(s)
+    w, b = run_train(s, inp, mask, dout, beta, counts_global, gather)
+    r = routing_of(s, b, mask)
+    check_stats(s, b, r, beta, counts_global)
+    fb = b.fwd
+    ref, _ = TR.forward(inp, s.alpha, s.k, mask, logits32=fb.logits.cpu().numpy())
+    assert_close_rel(to_f64(fb.out), ref, TOL, "out")
+    g = TR.backward(inp, s.alpha, r, dout, beta, counts_global)
+    S, T = int(r.offsets[-1]), s.T
+    F, Fs = s.F, s.Fs
+    gu = to_f64(b.gu)
+    if S:
+        assert_close_rel(gu[:s.S * 2 * F].reshape(s.S, 2 * F)[:S], g.gu_perm, TOL, "gu routed")
+    if Fs:
+        assert_close_rel(gu[s.S * 2 * F:].reshape(T, 2 * Fs), g.gu_shared, TOL, "gu shared")
+    if S:
+        assert_close_rel(to_f64(b.dy_perm)[:S], g.dy_perm, TOL, "dy_perm")
+        dgu = to_f64(b.dgu)
+        assert_close_rel(dgu[:s.S * 2 * F].reshape(s.S, 2 * F)[:S], g.dgu_perm, TOL, "dgu routed")
+        assert_close_rel(to_f64(b.dx_perm)[:S], g.dx_perm, TOL, "dx_perm")
+    if Fs:
+        assert_close_rel(to_f64(b.dgu)[s.S * 2 * F:].reshape(T, 2 * Fs), g.dgu_shared, TOL, "dgu shared")
+    assert_close_rel(b.dz.cpu().numpy().astype(np.float64), g.dz, TOL, "dz")
+    assert_close_rel(to_f64(b.dx), g.dx, TOL, "dx")
+    assert_close_rel(to_f64(b.dw_gate_up), g.dwgu, TOL, "dw_gate_up")
+    assert_close_rel(to_f64(b.dw_down), g.dwd, TOL, "dw_down")
+    if Fs:
+        assert_close_rel(to_f64(b.dws_gate_up), g.dwsgu, TOL, "dws_gate_up")
+        assert_close_rel(to_f64(b.dws_down), g.dwsd, TOL, "dws_down")
+    assert_close_rel(b.dw_router.cpu().numpy().astype(np.float64), g.dw_router, TOL, "dw_router")
+    assert_close_rel(b.dbias.cpu().numpy().astype(np.float64), g.dbias, TOL, "dbias")
+    # untouched experts get exactly zero
+    empty = np.nonzero(r.counts == 0)[0]
+    if empty.size:
+        assert float(b.dw_gate_up[empty].abs().max()) == 0.0 and float(b.dw_down[empty].abs().max()) == 0.0
+    # padding tokens: no logit gradient
+    pad = np.nonzero(mask == 0)[0]
+    if pad.size:
+        assert float(b.dz[pad].abs().max()) == 0.0
+    say(f"{s.name}: training pass within {TOL} of the oracle")
+    return inp, w, b, r
+
+
+# ------------------------------------------------------------------ small shapes, every element
+
+def test_small_with_padding_and_aux_loss():
+    full_parity(SMALL)
+
+
+def test_small_x_perm_mode():
+    full_parity(SMALL, gather=False)
+
+
+def test_small_global_counts():
+    counts_global = 3 * np.arange(1, SMALL.E + 1)
+    full_parity(SMALL, counts_global=counts_global)
+
+
+def test_small_without_aux_loss():
+    full_parity(SMALL, beta=0.0)
+
+
+EDGE = {
+    "no_padding": dict(pad_frac=0.0),
+    "no_shared": dict(Fs=0),
+    "k1": dict(k=1),
+    "T1": dict(T=1, pad_frac=0.0),
+    "E256_T70": dict(T=70, E=256, k=8, seq_len=32),
+    "wide_D512_rows256": dict(T=512, D=512, E=16, k=8),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_edge_shapes(case):
+    full_parity(configs.variant(SMALL, name=f"train_edge_{case}", **EDGE[case]))
+
+
+def test_all_padding():
+    s = configs.variant(SMALL, name="train_all_padding", T=40)
+    inp, w, b, r = full_parity(s, mask=np.zeros(40, np.uint8))
+    assert float(b.dw_gate_up.abs().max()) == 0.0 and float(b.dw_router.abs().max()) == 0.0
+
+
+def test_deterministic():
+    s = configs.variant(SMALL, name="train_determinism")
+    inp = StackedInputs(LayerInputs(s))
+    mask, dout = token_mask(s), dout_encoded(s)
+    outs = []
+    for rep in range(2):
+        _, b = run_train(s, inp, mask, dout, s.aux_coef)
+        outs.append([t.clone() for t in (b.fwd.out, b.dx, b.dz, b.dw_gate_up, b.dw_down, b.dws_gate_up,
+                                         b.dw_router, b.dbias, b.p, b.aux_loss)])
+    assert all(torch.equal(p, q) for p, q in zip(*outs))
+
+
+# ------------------------------------------------------------------ full size, sampled
+
+TRAIN_XS2 = configs.variant(configs.XS2_T4096, name="xs2_train_bf16_t4096_d2048", pad_frac=1 / 16)
+
+
+def test_xs2_training_sampled_parity():
+    s = TRAIN_XS2
+    inp = StackedInputs(LayerInputs(s))
+    mask, dout = token_mask(s), dout_encoded(s)
+    beta = s.aux_coef
+    w, b = run_train(s, inp, mask, dout, beta)
+    r = routing_of(s, b, mask)
+    check_stats(s, b, r, beta)
+    rng = np.random.default_rng(0)
+    pad = np.nonzero(mask == 0)[0]
+    toks = sorted(set(rng.choice(s.T, 24, replace=False).tolist()) | {0, s.T - 1} | set(pad[:3].tolist()))
+    say(f"oracle on {len(toks)} sampled tokens")
+    dz, dx = TR.token_grads(inp, s.alpha, r, dout, toks, beta)
+    assert_close_rel(b.dz.cpu().numpy()[toks].astype(np.float64), dz, TOL, "sampled dz")
+    assert_close_rel(to_f64(b.dx)[toks], dx, TOL, "sampled dx")
+    nz = np.nonzero(r.counts)[0]
+    experts = sorted({int(np.argmax(r.counts)), int(nz[np.argmin(r.counts[nz])]), int(rng.choice(nz))})
+    for e in experts:
+        say(f"oracle on expert {e} ({int(r.counts[e])} rows)")
+        dwgu, dwd, dgu, dy = TR.expert_grads(inp, s.alpha, r, dout, e)
+        assert_close_rel(to_f64(b.dw_gate_up[e]), dwgu, TOL, f"dw_gate_up[{e}]")
+        assert_close_rel(to_f64(b.dw_down[e]), dwd, TOL, f"dw_down[{e}]")
+        lo, hi = int(r.offsets[e]), int(r.offsets[e + 1])
+        assert_close_rel(to_f64(b.dgu)[:s.S * 2 * s.F].reshape(s.S, 2 * s.F)[lo:hi], dgu, TOL, f"dgu of {e}")
+        assert_close_rel(to_f64(b.dy_perm)[lo:hi], dy, TOL, f"dy of {e}")
+    # shared expert over all rows (dy = dout)
+    say("oracle on the shared expert")
+    x = O.widen(inp.x)
+    sh = inp.shared()
+    *_, dwsgu, dwsd = TR.expert_backward_rows(x, O.widen(sh[0]), O.widen(sh[1]), O.widen(dout))
+    assert_close_rel(to_f64(b.dws_gate_up), dwsgu, TOL, "dws_gate_up")
+    assert_close_rel(to_f64(b.dws_down), dwsd, TOL, "dws_down")
+    # router gradients: products of the GPU's own dz (checked on samples
+    # above) with x, in float64
+    dz16 = to_f64(b.dz16)[:, :s.E]
+    assert_close_rel(b.dw_router.cpu().numpy().astype(np.float64), dz16.T @ x, 1e-3, "dw_router = dz^T x")
+    dzf = b.dz.cpu().numpy().astype(np.float64)
+    assert_close_rel(b.dbias.cpu().numpy().astype(np.float64), dzf.sum(axis=0), 1e-5, "dbias = sum dz")
+    say("xs2 training pass: sampled parity within tolerance")
