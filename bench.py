@@ -1,6 +1,6 @@
 """Single-GPU benchmark of the MoE feed-forward layer through libmoe's C ABI.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--train]
 
 One step = one whole layer pass over one batch: moe_route, moe_permute,
 moe_grouped_gate_up, moe_grouped_down, moe_combine, all enqueued on one HIP
@@ -15,6 +15,10 @@ tokens/s of the layer, plus
                 against the MI355X peak that bounds it;
   cpu_baseline  the CPU oracle (fp64 NumPy, self-contained routing) timed on the
                 host cores on the same workload.
+
+With --train, one step is the training pass instead (forward keeping the
+activations the backward needs, then every gradient), on the padded XS.2
+training batch by default; its roofline entry is the weight-gradient kernel.
 
 Synthetic seeded inputs; random-init weights of the layer's shape.
 """
@@ -136,6 +140,156 @@ def cpu_oracle_baseline(s, inp_host, target_s: float = 12.0, fp8: bool = False):
             "sample": sample, "seconds": round(el, 3)}
 
 
+def wgrad_work(s: configs.MoEShape, routed_rows: int):
+    """Algorithmic FLOPs and HBM bytes of one weight-gradient launch
+    (moe_weight_grads): every gradient written once (bf16 experts, fp32
+    router) and every input tensor read once (x, [dg | du], dy, dout, h and the
+    bf16 logit gradient; R = routed rows, T = tokens)."""
+    R, T, D, F, Fs, E = routed_rows, s.T, s.D, s.F, s.Fs, s.E
+    flops = 2.0 * R * (2 * F * D + D * F) + 2.0 * T * (2 * Fs * D + D * Fs) + 2.0 * T * E * D
+    out = (E * (2 * F * D + D * F) + (2 * Fs * D + D * Fs)) * 2 + E * D * 4
+    inp = (T * D + (R * 2 * F + T * 2 * Fs) + R * D + T * D + (R * F + T * Fs) + T * 256) * 2
+    return flops, float(out + inp)
+
+
+def train_flops(s: configs.MoEShape, routed_rows: int) -> float:
+    """FLOPs of one training pass: the forward (router, both expert GEMMs,
+    shared expert) and, for each of its products, the two backward products."""
+    R, T = routed_rows, s.T
+    fwd = 2.0 * T * s.D * s.E + 6.0 * R * s.D * s.F + 6.0 * T * s.D * s.Fs
+    return 3.0 * fwd
+
+
+def cpu_train_baseline(s, inp_host, mask, dout, target_s: float = 12.0):
+    """Times the training oracle (fp64 forward + backward) on a token sample."""
+    from oracle import moe_oracle as O
+    from oracle import train_oracle as TR
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+
+    class Sub:
+        def __init__(self, n):
+            self.x = inp_host["x"][:n]
+            self.w_router = inp_host["w_router"]
+            self.bias = inp_host["bias"]
+
+        def expert(self, e):
+            return inp_host["wgu"][e], inp_host["wd"][e]
+
+        def shared(self):
+            return inp_host["shared"]
+
+    def one(n):
+        sub = Sub(n)
+        out, r = TR.forward(sub, s.alpha, s.k, mask[:n])
+        TR.backward(sub, s.alpha, r, dout[:n], s.aux_coef)
+
+    n0 = min(s.T, 128)
+    t0 = time.perf_counter()
+    one(n0)
+    probe = time.perf_counter() - t0
+    n = min(s.T, max(n0, int(n0 * target_s / probe)))
+    passes, tokens, t0 = 0, 0, time.perf_counter()
+    while True:
+        one(n)
+        passes += 1
+        tokens += n
+        el = time.perf_counter() - t0
+        if el >= min(target_s, 10.0) or passes >= 8:
+            break
+    sample = (f"fp64 training oracle (masked forward with its own routing, then the backward of every "
+              f"expert touched, shared expert and router) over the first {n} of {s.T} tokens, "
+              f"{passes} pass(es), weights already in host memory")
+    return {"value": tokens / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample, "seconds": round(el, 3)}
+
+
+def train_main(args):
+    """One step = the training pass: masked route, permute, load statistics,
+    gate/up keeping the pre-activations, down, combine; then the combine
+    backward, dh and SwiGLU backward, dx, weight and bias gradients."""
+    import torch
+    from mixture_experts_transformer_moe_amd import binding
+    from mixture_experts_transformer_moe_amd.inputs import LayerInputs, dout_encoded, token_mask
+
+    s = configs.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = LayerInputs(s)
+    wgu, wd = inp.all_experts()
+    host = {"x": inp.x, "w_router": inp.w_router, "bias": inp.bias, "wgu": wgu, "wd": wd,
+            "shared": inp.shared()}
+    w = binding.upload_train_weights(s, inp.w_router, inp.bias, wgu, wd, host["shared"], dev)
+    x = binding.to_device(inp.x, s, dev)
+    mask_h, dout_h = token_mask(s), dout_encoded(s)
+    mask = torch.from_numpy(mask_h).to(dev)
+    dout = binding.to_device(dout_h, s, dev)
+    b = binding.alloc_train_buffers(s, mask, dev, with_x_perm=args.x_perm)
+    c = binding.make_shape(s)
+    stream = torch.cuda.current_stream(dev)
+    fb = b.fwd
+
+    def step(ev=None):
+        binding.train_forward(s, x, w, b, s.aux_coef, None, stream)
+        binding.moe_combine_backward(c, dout, fb.y_perm, fb.slot_of, fb.topk_idx, fb.topk_w, fb.logits,
+                                     b.aux_coef, b.dy_perm, b.dz, b.dz16, stream)
+        binding.moe_grouped_backward_h(c, b.dy_perm, dout, fb.offsets, w.w_down_t, w.ws_down_t, b.gu,
+                                       b.dh, b.dgu, stream)
+        binding.moe_grouped_backward_x(c, b.dgu, fb.offsets, w.w_gate_up_t, w.ws_gate_up_t, b.dz16,
+                                       w.w_router_t, fb.slot_of, b.dx_perm, b.dx_shared, b.dx_router,
+                                       b.dx, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        binding.moe_weight_grads(c, x, fb.sorted_token, fb.x_perm, fb.offsets, b.dgu, b.dy_perm, dout,
+                                 fb.h, b.dz16, b.dw_gate_up, b.dw_down, b.dws_gate_up, b.dws_down,
+                                 b.dw_router, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        binding.moe_bias_grad(c, b.dz, b.dbias, b.train_ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timed = list(range(0, args.steps, EV_EVERY))
+    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in timed}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs.get(i))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    wg_ms = float(np.mean([a.elapsed_time(z) for a, z in evs.values()]))
+
+    routed_rows = int(fb.offsets[-1].item())
+    flops, nbytes = wgrad_work(s, routed_rows)
+    achieved = nbytes / (wg_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "kernel": "wgrad_kernel (moe_weight_grads)", "kernel_ms": round(wg_ms, 4),
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "mfma_tflops": round(flops / (wg_ms * 1e-3) / 1e12, 1)}
+    ms = elapsed * 1e3 / args.steps
+    cpu = None if args.no_cpu_baseline else cpu_train_baseline(s, host, mask_h, dout_h)
+    line = {
+        "metric": "MoE-layer training tokens/s (forward + backward) at 1 MI355X",
+        "value": round(s.T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.dtype,
+        "data": "synthetic",
+        "config": {"workload": s.name, "tokens": s.T, "routed_tokens": routed_rows // s.k,
+                   "d_model": s.D, "experts": s.E, "top_k": s.k, "expert_width": s.F,
+                   "shared_width": s.Fs, "alpha": s.alpha, "aux_coef": s.aux_coef,
+                   "a_rows": "x_perm" if args.x_perm else "gather", "parallelism": "single-gpu"},
+        "train_tflops": round(train_flops(s, routed_rows) / (ms * 1e-3) / 1e12, 1),
+        "aux_loss": float(b.aux_loss.item()),
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +303,9 @@ def main():
     ap.add_argument("--fp8-weights", action="store_true",
                     help="expert weights in FP8 (E4M3, per-row scales; moe_quantize_weights_fp8) "
                          "and the FP8 grouped GEMMs")
+    ap.add_argument("--train", action="store_true",
+                    help="time the training pass (forward keeping activations, then the backward "
+                         "and every gradient) on the training workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB device to device "
@@ -158,6 +315,12 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's "
               "multi-GPU sharding is a design note, not a measured path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.train:
+        if args.workload == configs.BENCH_WORKLOAD:
+            args.workload = configs.XS2_TRAIN_T4096.name
+        train_main(args)
+        return
 
     import torch
     from mixture_experts_transformer_moe_amd import binding

@@ -265,7 +265,7 @@ int moe_combine(const moe_shape* shape, const void* y_perm, const void* y_shared
  * moe_grouped_gate_up_train, moe_grouped_down, moe_combine.  Backward of
  *   J = <dout, out> + L_aux
  * with the top-k selection held fixed: moe_combine_backward,
- * moe_grouped_backward_h, moe_grouped_backward_x, moe_weight_grads.
+ * moe_grouped_backward_h, moe_grouped_backward_x, moe_weight_grads, moe_bias_grad.
  * Readings (the pages state none of these formulas):
  *   - load balancing is the global-batch auxiliary loss of Qiu et al. ("Laguna
  *     M.1/XS.2 Technical Report", Key claims, XS.2 routing item): over the N
@@ -283,7 +283,7 @@ int moe_combine(const moe_shape* shape, const void* y_perm, const void* y_shared
  * expert order, then the T shared rows.
  * ------------------------------------------------------------------------- */
 
-/* Bytes of workspace moe_load_stats and moe_weight_grads (bias gradient) need. */
+/* Bytes of workspace moe_load_stats and moe_bias_grad need. */
 size_t moe_train_workspace_bytes(const moe_shape* shape);
 
 /* Bytes of moe_pack_weights_transposed's output: count * cols * k_padded * 2,
@@ -357,14 +357,18 @@ int moe_grouped_backward_x(const moe_shape* shape, const void* dgu, const int32_
  *   dw_down    [E, D, F]  bf16 = dy^T h
  *   dws_gate_up [2Fs, D], dws_down [D, Fs] bf16: the shared expert over all T
  *              rows (dy = dout); unused when Fs == 0
- *   dw_router  [E, D] fp32 = dz^T x, or NULL to skip
- *   dbias      [E] fp32 = sum_t dz_t, or NULL to skip (needs the workspace)
+ *   dw_router  [E, D] fp32 = dz^T x (from dz_bf16), or NULL to skip
  *   x_perm may be NULL (rows then come from x through sorted_token). */
 int moe_weight_grads(const moe_shape* shape, const void* x, const int32_t* sorted_token,
                      const void* x_perm, const int32_t* offsets, const void* dgu, const void* dy_perm,
-                     const void* dout, const void* h, const void* dz_bf16, const float* dz,
-                     void* dw_gate_up, void* dw_down, void* dws_gate_up, void* dws_down, float* dw_router,
-                     float* dbias, void* workspace, size_t workspace_bytes, void* stream);
+                     const void* dout, const void* h, const void* dz_bf16, void* dw_gate_up, void* dw_down,
+                     void* dws_gate_up, void* dws_down, float* dw_router, void* stream);
+
+/* Router bias gradient: dbias [E] fp32 = sum over tokens of dz [T, E] (fp32,
+ * from moe_combine_backward), summed in a fixed order.
+ *   workspace >= moe_train_workspace_bytes */
+int moe_bias_grad(const moe_shape* shape, const float* dz, float* dbias, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

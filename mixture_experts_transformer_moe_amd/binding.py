@@ -31,7 +31,7 @@ EXPORTS = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_
            "moe_route_masked", "moe_train_workspace_bytes", "moe_packed_transposed_bytes",
            "moe_pack_weights_transposed", "moe_load_stats", "moe_grouped_gate_up_train",
            "moe_combine_backward", "moe_grouped_backward_h", "moe_grouped_backward_x",
-           "moe_weight_grads")
+           "moe_weight_grads", "moe_bias_grad")
 
 
 class moe_shape(ctypes.Structure):
@@ -116,7 +116,9 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_backward_x.restype = ctypes.c_int
         L.moe_grouped_backward_x.argtypes = [_SP] + [_P] * 12
         L.moe_weight_grads.restype = ctypes.c_int
-        L.moe_weight_grads.argtypes = [_SP] + [_P] * 17 + [ctypes.c_size_t, _P]
+        L.moe_weight_grads.argtypes = [_SP] + [_P] * 15
+        L.moe_bias_grad.restype = ctypes.c_int
+        L.moe_bias_grad.argtypes = [_SP, _P, _P, _P, ctypes.c_size_t, _P]
         _lib = L
     return _lib
 
@@ -470,15 +472,17 @@ def moe_grouped_backward_x(shape, dgu, offsets, w_gate_up_t, ws_gate_up_t, dz_bf
                                         _stream(stream)), "moe_grouped_backward_x")
 
 
-def moe_weight_grads(shape, x, sorted_token, x_perm, offsets, dgu, dy_perm, dout, h, dz_bf16, dz,
-                     dw_gate_up, dw_down, dws_gate_up, dws_down, dw_router, dbias, workspace,
-                     stream=None):
+def moe_weight_grads(shape, x, sorted_token, x_perm, offsets, dgu, dy_perm, dout, h, dz_bf16,
+                     dw_gate_up, dw_down, dws_gate_up, dws_down, dw_router, stream=None):
     _check(lib().moe_weight_grads(ctypes.byref(shape), _ptr(x), _ptr(sorted_token), _ptr(x_perm),
                                   _ptr(offsets), _ptr(dgu), _ptr(dy_perm), _ptr(dout), _ptr(h),
-                                  _ptr(dz_bf16), _ptr(dz), _ptr(dw_gate_up), _ptr(dw_down),
-                                  _ptr(dws_gate_up), _ptr(dws_down), _ptr(dw_router), _ptr(dbias),
-                                  _ptr(workspace), _nbytes(workspace), _stream(stream)),
-           "moe_weight_grads")
+                                  _ptr(dz_bf16), _ptr(dw_gate_up), _ptr(dw_down), _ptr(dws_gate_up),
+                                  _ptr(dws_down), _ptr(dw_router), _stream(stream)), "moe_weight_grads")
+
+
+def moe_bias_grad(shape, dz, dbias, workspace, stream=None):
+    _check(lib().moe_bias_grad(ctypes.byref(shape), _ptr(dz), _ptr(dbias), _ptr(workspace),
+                               _nbytes(workspace), _stream(stream)), "moe_bias_grad")
 
 
 @dataclass
@@ -588,6 +592,6 @@ def train_backward(s: MoEShape, x: torch.Tensor, dout: torch.Tensor, w: TrainWei
     moe_grouped_backward_x(c, b.dgu, fb.offsets, w.w_gate_up_t, w.ws_gate_up_t, b.dz16, w.w_router_t,
                            fb.slot_of, b.dx_perm, b.dx_shared, b.dx_router, b.dx, stream)
     moe_weight_grads(c, x, fb.sorted_token, fb.x_perm, fb.offsets, b.dgu, b.dy_perm, dout, fb.h, b.dz16,
-                     b.dz, b.dw_gate_up, b.dw_down, b.dws_gate_up, b.dws_down, b.dw_router, b.dbias,
-                     b.train_ws, stream)
+                     b.dw_gate_up, b.dw_down, b.dws_gate_up, b.dws_down, b.dw_router, stream)
+    moe_bias_grad(c, b.dz, b.dbias, b.train_ws, stream)
     return b.dx

@@ -63,6 +63,13 @@ class MoEShape:
         return router + routed + shared
 
 
+def variant(base: MoEShape, **kw) -> MoEShape:
+    """Same recipe with some fields changed (used for edge cases)."""
+    d = base.as_dict()
+    d.update(kw)
+    return MoEShape(**d)
+
+
 TINY_F32 = MoEShape("tiny_f32_t64", T=64, D=256, E=16, k=4, F=128, Fs=128, alpha=2.5,
                     dtype="f32", seed=0, x_recipe="normal", x_std=0.02)
 XS2_T4096 = MoEShape("xs2_bf16_t4096_d2048", T=4096, D=2048, E=256, k=8, F=512, Fs=512,
@@ -81,9 +88,16 @@ PREFILL_OUTLIER_T32768 = MoEShape("prefill_outlier_bf16_t32768_d2048", T=32768, 
 M1_TOP16_T8192 = MoEShape("m1_top16_bf16_t8192_d4096", T=8192, D=4096, E=256, k=16, F=1024,
                           Fs=1024, alpha=1.0, dtype="bf16", seed=5)
 
+# The training pass at the XS.2 shape: one padded batch (padding tokens at the
+# ends of 1024-token sequences, 1/16 of the batch on average; "Laguna M.1/XS.2
+# Technical Report", thread on the report: padding tokens are not routed) and
+# an auxiliary-loss coefficient of 1e-3 (the pages give none).
+XS2_TRAIN_T4096 = variant(XS2_T4096, name="xs2_train_bf16_t4096_d2048", pad_frac=1 / 16,
+                          aux_coef=1e-3)
+
 WORKLOADS: Dict[str, MoEShape] = {s.name: s for s in
                                   (TINY_F32, XS2_T4096, M1_T8192, DECODE_SKEW_T32,
-                                   PREFILL_OUTLIER_T32768, M1_TOP16_T8192)}
+                                   PREFILL_OUTLIER_T32768, M1_TOP16_T8192, XS2_TRAIN_T4096)}
 
 # The single-GPU benchmark workload: the XS.2-shaped layer.
 BENCH_WORKLOAD = XS2_T4096.name
@@ -93,8 +107,3 @@ def get(name: str) -> MoEShape:
     return WORKLOADS[name]
 
 
-def variant(base: MoEShape, **kw) -> MoEShape:
-    """Same recipe with some fields changed (used for edge cases)."""
-    d = base.as_dict()
-    d.update(kw)
-    return MoEShape(**d)

@@ -522,9 +522,8 @@ int moe_grouped_backward_x(const moe_shape* shape, const void* dgu, const int32_
 
 int moe_weight_grads(const moe_shape* shape, const void* x, const int32_t* sorted_token,
                      const void* x_perm, const int32_t* offsets, const void* dgu, const void* dy_perm,
-                     const void* dout, const void* h, const void* dz_bf16, const float* dz,
-                     void* dw_gate_up, void* dw_down, void* dws_gate_up, void* dws_down, float* dw_router,
-                     float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+                     const void* dout, const void* h, const void* dz_bf16, void* dw_gate_up, void* dw_down,
+                     void* dws_gate_up, void* dws_down, float* dw_router, void* stream) {
   if (int r = check_train_shape(shape)) return r;
   const moe_shape& s = *shape;
   // with no tokens every gradient is zero and no input is read
@@ -538,7 +537,6 @@ int moe_weight_grads(const moe_shape* shape, const void* x, const int32_t* sorte
     NEED_PTR(h);
     if (s.Fs > 0) NEED_PTR(dout);
     if (dw_router) NEED_PTR(dz_bf16);
-    if (dbias) NEED_PTR(dz);
   }
   NEED_PTR(dw_gate_up);
   NEED_PTR(dw_down);
@@ -547,19 +545,22 @@ int moe_weight_grads(const moe_shape* shape, const void* x, const int32_t* sorte
     NEED_PTR(dws_down);
   }
   OPT_PTR(dw_router);
-  OPT_PTR(dbias);
-  if (dbias)
-    if (int r = check_workspace(workspace, workspace_bytes, moe::train_workspace_bytes(s))) return r;
   using moe::bf16_t;
-  const hipStream_t st = as_stream(stream);
-  hipError_t e = moe::launch_wgrad(
+  return launched(moe::launch_wgrad(
       s, static_cast<const bf16_t*>(x), sorted_token, static_cast<const bf16_t*>(x_perm),
       static_cast<const bf16_t*>(dgu), static_cast<const bf16_t*>(dy_perm), static_cast<const bf16_t*>(h),
       static_cast<const bf16_t*>(dout), static_cast<const bf16_t*>(dz_bf16), offsets,
       static_cast<bf16_t*>(dw_gate_up), static_cast<bf16_t*>(dw_down), static_cast<bf16_t*>(dws_gate_up),
-      static_cast<bf16_t*>(dws_down), dw_router, st);
-  if (e == hipSuccess && dbias) e = moe::launch_colsum(s, dz, dbias, workspace, st);
-  return launched(e);
+      static_cast<bf16_t*>(dws_down), dw_router, as_stream(stream)));
+}
+
+int moe_bias_grad(const moe_shape* shape, const float* dz, float* dbias, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (shape->T > 0) NEED_PTR(dz);
+  NEED_PTR(dbias);
+  if (int r = check_workspace(workspace, workspace_bytes, moe::train_workspace_bytes(*shape))) return r;
+  return launched(moe::launch_colsum(*shape, dz, dbias, workspace, as_stream(stream)));
 }
 
 }  // extern "C"

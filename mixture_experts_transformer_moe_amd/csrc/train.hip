@@ -26,7 +26,7 @@ namespace {
 
 constexpr int kMaxK = 16;
 constexpr int kDzLd = 256;        // row stride of the bf16 logit gradient (E padded to 256)
-constexpr int kStatRows = 64;     // token rows per block of the column sums
+constexpr int kStatRows = 16;     // token rows per block of the column sums
 
 __device__ __forceinline__ void load8(const bf16_t* p, float* v) {
   const u32x4 q = *reinterpret_cast<const u32x4*>(p);
@@ -309,13 +309,27 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const float* __rest
   part[static_cast<size_t>(blockIdx.x) * E + e] = acc;
 }
 
+// sum_b part[b][e] for b = 0, 1, ..., nb - 1 in that order; the loads of 8
+// blocks are issued together ahead of their adds
+__device__ __forceinline__ float ordered_sum(const float* __restrict__ part, int nb, int E, int e) {
+  float acc = 0.f;
+  int b = 0;
+  for (; b + 8 <= nb; b += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[static_cast<size_t>(b + u) * E + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; b < nb; ++b) acc += part[static_cast<size_t>(b) * E + e];
+  return acc;
+}
+
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int nb,
                                                            int E, float* __restrict__ out) {
   const int e = threadIdx.x;
   if (e >= E) return;
-  float acc = 0.f;
-  for (int b = 0; b < nb; ++b) acc += part[static_cast<size_t>(b) * E + e];
-  out[e] = acc;
+  out[e] = ordered_sum(part, nb, E, e);
 }
 
 // f, p, the auxiliary loss and its per-expert coefficients c = beta E f / N.
@@ -330,9 +344,7 @@ __global__ __launch_bounds__(256) void load_stats_final_kernel(
   const float n_slots = block_sum(cl, red4);        // counts are exact in fp32 below 2^24
   const float g_slots = block_sum(cg, red4);
   const float N = n_slots / static_cast<float>(k);
-  float psum = 0.f;
-  if (e < E)
-    for (int b = 0; b < nb; ++b) psum += part[static_cast<size_t>(b) * E + e];
+  const float psum = e < E ? ordered_sum(part, nb, E, e) : 0.f;
   const float pe = N > 0.f ? psum / N : 0.f;
   const float fe = g_slots > 0.f ? cg / g_slots : 0.f;
   const float l = block_sum(fe * pe, red4);

@@ -11,35 +11,46 @@
 // bf16 operands, fp32 accumulation; expert gradients rounded once to bf16,
 // the router's kept in fp32.  A group with no rows gets zeros.
 //
-// Design.  The reduction runs over token rows, which are the strided
-// dimension of both operands, while a 32x32x16 MFMA wants 8 consecutive K
-// values per lane.  Each stage therefore moves 64 token rows of a 128-column
-// A tile and a 128-column B tile through LDS transposed: a thread loads 16
-// bytes (8 columns) from each of 4 consecutive rows, pairs the rows' values
-// column by column with v_perm, and writes 8-byte [column][4 rows] pieces
-// (ds_write_b64, 16 lanes = one contiguous 128-byte run); the fragments then
-// come back as single 16-byte LDS reads.  LDS rows are 72 elements (144 bytes)
-// long, so the 8 lanes of a 16-byte read hit 8 disjoint bank groups.  A tile
-// is 128 x 128 outputs, 4 waves of 64 x 64 (2 x 2 MFMA blocks); the MFMA's
-// first operand is the B fragment, so a lane holds consecutive output columns
-// and stores 16 bytes after a lane-pair swap, as in the forward GEMMs.  Two
-// LDS stages (72 KB) let the next stage's loads fly during the MFMAs.
+// Design.  The reduction runs over token rows, the strided dimension of both
+// operands, while a 32x32x16 MFMA wants 8 consecutive K values per lane.
+// Stages of 32 token rows of a 256-column A tile and a 128-column B tile go
+// from global memory straight into LDS (global_load_lds_dwordx4, no
+// registers), row-major, the 16-byte units of row r XOR-swizzled by
+// 4 (r mod 4); gfx950's transposing LDS read (ds_read_b64_tr_b16) then hands
+// each lane 4 consecutive rows of one column, two reads per MFMA fragment.  In
+// a group of 16 lanes that read returns to lane 4a + b element b of the 8-byte
+// pieces addressed by lanes a, a + 4, a + 8 and a + 12, so lane j addresses
+// row k0 + j / 4, columns c0 + 4 (j mod 4) .. + 3, and lane i receives rows
+// k0 .. k0 + 3 of column c0 + i; with the swizzle the 16 lanes of a read hit
+// distinct banks.  Three stages are in flight (72 KB, 2 workgroups per CU):
+// the tiles are short (an expert's ~100-200 rows are a few stages), so the
+// kernel is bound by the latency of its loads unless several stages fly at
+// once.  Rows past the group's end load its last row again and the A values
+// of the last stage's rows past the end are zeroed, so they add nothing.
+// A tile is 256 x 128 outputs, 8 waves of 64 x 64 (2 x 2 MFMA blocks); the
+// MFMA's first operand is the B fragment, so a lane holds consecutive output
+// columns and stores 16 bytes after a lane-pair swap, as in the forward GEMMs.
+// Gathered token ids (x rows of a routed expert) come through scalar loads,
+// 4 per wave and stage, so that no vector wait drains the stages in flight.
 //
 // Schedule: the long groups (shared expert, router: all T rows) and the
 // routed experts' tiles are dealt to the 8 XCDs so that each XCD gets an
 // equal share of the long tiles first, then the tiles of a contiguous run of
 // experts (blocks b and b + 8 run on the same XCD), so an expert's rows are
 // read into one L2.
-#include "moe_internal.h"
+#include "lds_dma.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTile = 128;            // output tile edge (M and N)
-constexpr int kKC = 64;               // token rows per stage
-constexpr int kRowE = 72;             // LDS row length in elements (64 rows + 8 pad)
-constexpr int kOpElems = kTile * kRowE;
-constexpr int kStageElems = 2 * kOpElems;   // A then B
+constexpr int kBM = 256;              // output tile rows (A columns)
+constexpr int kBN = 128;              // output tile columns (B columns)
+constexpr int kKC = 32;               // token rows per stage
+constexpr int kNS = 3;                // stages in flight
+constexpr int kAElems = kKC * kBM;
+constexpr int kBElems = kKC * kBN;
+constexpr int kStageElems = kAElems + kBElems;
+constexpr int kThreadsW = 512;
 constexpr int kXcds = 8;
 constexpr int kDzLd = 256;
 
@@ -77,59 +88,84 @@ struct TileJob {
   bool f32;
 };
 
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs g) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kStageElems];
+__device__ __forceinline__ int unit_swz(int r) { return 4 * (r & 3); }
+
+// element offset of (row, col) in a stage operand of `units` 16-byte units per row
+template <int kUnits>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * (8 * kUnits) + (((col >> 3) ^ unit_swz(row)) << 3) + (col & 7);
+}
+
+// MFMA fragment of columns c0 .. c0 + 31, rows k0 .. k0 + 15 (lane l: column
+// c0 + l mod 32, rows k0 + 8 (l / 32) + 0..7)
+template <int kUnits>
+__device__ __forceinline__ bf16x8 tr_fragment(const bf16_t* t, int c0, int k0, int lane) {
+  const int grp = lane >> 4, j = lane & 15;
+  const int col = c0 + 16 * (grp & 1) + 4 * (j & 3);
+  const int row = k0 + 8 * (grp >> 1) + (j >> 2);
+  typedef __attribute__((address_space(3))) v4i16 lds_v4;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4*)(reinterpret_cast<__attribute__((address_space(3))) bf16_t*>(
+          static_cast<uint32_t>(reinterpret_cast<uintptr_t>(t + tile_off<kUnits>(row, col))))));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4*)(reinterpret_cast<__attribute__((address_space(3))) bf16_t*>(
+          static_cast<uint32_t>(reinterpret_cast<uintptr_t>(t + tile_off<kUnits>(row + 4, col))))));
+  const v4i16 v[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__global__ __launch_bounds__(kThreadsW, 2) void wgrad_kernel(WgradArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[kNS * kStageElems];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- which tile: block b runs on XCD b % 8 as the (b / 8)-th of its blocks
   const int xcd = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
   TileJob j{};
-  int m0, n0;
   if (i < g.long_per_xcd) {
     const int li = xcd + kXcds * i;
     if (li >= g.n_router + g.n_sgu + g.n_sd) return;
     j.r0 = 0;
     j.r1 = g.T;
     j.gathered = false;
+    int m0, n0;
     if (li < g.n_router) {
-      const int nt = g.D / kTile;
-      m0 = (li / nt) * kTile;
-      n0 = (li % nt) * kTile;
+      const int nt = g.D / kBN;
+      m0 = (li / nt) * kBM;
+      n0 = (li % nt) * kBN;
       j.a = g.dz16 + m0;
       j.lda = kDzLd;
       j.b = g.x + n0;
       j.ldb = g.D;
       j.out = g.dwr + static_cast<size_t>(m0) * g.D + n0;
       j.ldo = g.D;
-      j.m_valid = min(kTile, g.E - m0);
+      j.m_valid = min(kBM, g.E - m0);
       j.f32 = true;
     } else if (li < g.n_router + g.n_sgu) {
-      const int t = li - g.n_router, nt = g.D / kTile;
-      m0 = (t / nt) * kTile;
-      n0 = (t % nt) * kTile;
+      const int t = li - g.n_router, nt = g.D / kBN;
+      m0 = (t / nt) * kBM;
+      n0 = (t % nt) * kBN;
       j.a = g.dgu + static_cast<size_t>(g.S) * 2 * g.F + m0;
       j.lda = 2 * g.Fs;
       j.b = g.x + n0;
       j.ldb = g.D;
       j.out = g.dwsgu + static_cast<size_t>(m0) * g.D + n0;
       j.ldo = g.D;
-      j.m_valid = kTile;
+      j.m_valid = kBM;
       j.f32 = false;
     } else {
-      const int t = li - g.n_router - g.n_sgu, nt = g.Fs / kTile;
-      m0 = (t / nt) * kTile;
-      n0 = (t % nt) * kTile;
+      const int t = li - g.n_router - g.n_sgu, nt = g.Fs / kBN;
+      m0 = (t / nt) * kBM;
+      n0 = (t % nt) * kBN;
       j.a = g.dout + m0;
       j.lda = g.D;
       j.b = g.h + static_cast<size_t>(g.S) * g.F + n0;
       j.ldb = g.Fs;
       j.out = g.dwsd + static_cast<size_t>(m0) * g.Fs + n0;
       j.ldo = g.Fs;
-      j.m_valid = kTile;
+      j.m_valid = kBM;
       j.f32 = false;
     }
   } else {
@@ -140,12 +176,11 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs g) {
     const int t = ri % tpe;
     j.r0 = g.T > 0 ? min(max(g.offsets[e], 0), g.S) : 0;
     j.r1 = g.T > 0 ? min(max(g.offsets[e + 1], j.r0), g.S) : 0;
-    j.m_valid = kTile;
+    j.m_valid = kBM;
     j.f32 = false;
     if (t < g.tiles_gu) {
-      const int nt = g.D / kTile;
-      m0 = (t / nt) * kTile;
-      n0 = (t % nt) * kTile;
+      const int nt = g.D / kBN;
+      const int m0 = (t / nt) * kBM, n0 = (t % nt) * kBN;
       j.a = g.dgu + m0;
       j.lda = 2 * g.F;
       j.gathered = g.x_perm == nullptr;
@@ -154,9 +189,8 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs g) {
       j.out = g.dwgu + (static_cast<size_t>(e) * 2 * g.F + m0) * g.D + n0;
       j.ldo = g.D;
     } else {
-      const int u = t - g.tiles_gu, nt = g.F / kTile;
-      m0 = (u / nt) * kTile;
-      n0 = (u % nt) * kTile;
+      const int u = t - g.tiles_gu, nt = g.F / kBN;
+      const int m0 = (u / nt) * kBM, n0 = (u % nt) * kBN;
       j.a = g.dy + m0;
       j.lda = g.D;
       j.gathered = false;
@@ -166,40 +200,44 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs g) {
       j.ldo = g.F;
     }
   }
-  (void)m0;
-  (void)n0;
 
-  // ---- stage loads: thread (kq, seg) takes rows 4 kq .. 4 kq + 3 of the
-  // stage and columns 8 seg .. 8 seg + 7 of both operands
-  const int kq = tid & 15, seg = tid >> 4;
-  u32x4 ra[4], rb[4];
-  auto load_stage = [&](int r_first) {
+  // ---- stage loads: wave w issues A loads 2w and 2w + 1 (1 KB each = two
+  // 512-byte A rows) and B load w (four 256-byte B rows) of every stage
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  const int nch = (j.r1 - j.r0 + kKC - 1) / kKC;
+  auto issue = [&](int c) {
+    const int slot = c % kNS;
+    const uint32_t base = lds0 + static_cast<uint32_t>(slot * kStageElems * 2);
+    const int rbase = j.r0 + c * kKC;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = r_first + 4 * kq + q;
-      const bool in = r < j.r1;
-      const int rr = in ? r : j.r0;          // any row of the group: not used
-      int brow = rr;
-      if (j.gathered) brow = min(max(g.gather[rr], 0), g.T - 1);
-      const u32x4 va = *reinterpret_cast<const u32x4*>(j.a + static_cast<size_t>(rr) * j.lda + 8 * seg);
-      const u32x4 vb = *reinterpret_cast<const u32x4*>(j.b + static_cast<size_t>(brow) * j.ldb + 8 * seg);
-      ra[q] = in ? va : u32x4{0u, 0u, 0u, 0u};
-      rb[q] = in ? vb : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < 2; ++q) {
+      const int P = 64 * (2 * wave + q) + lane;          // A slot: row P / 32, unit slot P % 32
+      const int r = P >> 5;
+      const int u = (P & 31) ^ unit_swz(r);
+      const int row = min(rbase + r, j.r1 - 1);
+      dma16(j.a + static_cast<size_t>(row) * j.lda + 8 * u,
+            __builtin_amdgcn_readfirstlane(base + static_cast<uint32_t>((2 * wave + q) * 1024)));
     }
-  };
-  // transposed write: column c = 8 seg + 2 d + h of the tile, rows 4 kq .. 4 kq + 3
-  auto store_stage = [&](bf16_t* st) {
+    {
+      const int P = 64 * wave + lane;                    // B slot: row P / 16, unit slot P % 16
+      const int r = P >> 4;
+      const int u = (P & 15) ^ unit_swz(r);
+      int row = min(rbase + r, j.r1 - 1);
+      if (j.gathered) {
+        // the wave's 4 rows: token ids by scalar loads
+        const __attribute__((address_space(4))) int32_t* gt =
+            (const __attribute__((address_space(4))) int32_t*)(g.gather);
+        const int rw = rbase + 4 * wave;
+        int id[4];
 #pragma unroll
-    for (int op = 0; op < 2; ++op) {
-      const u32x4* v = op == 0 ? ra : rb;
-      bf16_t* base = st + op * kOpElems + 4 * kq;
+        for (int k = 0; k < 4; ++k) id[k] = gt[min(rw + k, j.r1 - 1)];
+        int tok = id[0];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint2 lo = make_uint2(lo_pair(v[0][d], v[1][d]), lo_pair(v[2][d], v[3][d]));
-        const uint2 hi = make_uint2(hi_pair(v[0][d], v[1][d]), hi_pair(v[2][d], v[3][d]));
-        *reinterpret_cast<uint2*>(base + (8 * seg + 2 * d) * kRowE) = lo;
-        *reinterpret_cast<uint2*>(base + (8 * seg + 2 * d + 1) * kRowE) = hi;
+        for (int k = 1; k < 4; ++k) tok = (lane >> 4) == k ? id[k] : tok;
+        row = min(max(tok, 0), g.T - 1);
       }
+      dma16(j.b + static_cast<size_t>(row) * j.ldb + 8 * u,
+            __builtin_amdgcn_readfirstlane(base + static_cast<uint32_t>(kAElems * 2 + wave * 1024)));
     }
   };
 
@@ -209,27 +247,36 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs g) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{0.f};
 
-  const int wm = 64 * (wave & 1), wn = 64 * (wave >> 1);
-  const int nch = (j.r1 - j.r0 + kKC - 1) / kKC;
-  if (nch > 0) {
-    load_stage(j.r0);
-    store_stage(lds);
-    __syncthreads();
-  }
+  const int wm = 64 * (wave & 3), wn = 64 * (wave >> 2);
+#pragma unroll
+  for (int c = 0; c < kNS - 1; ++c)
+    if (c < nch) issue(c);
   for (int c = 0; c < nch; ++c) {
-    const bool more = c + 1 < nch;
-    if (more) load_stage(j.r0 + (c + 1) * kKC);
-    const bf16_t* st = lds + (c & 1) * kStageElems;
+    // stage c landed: the stages issued after it (3 loads each per wave) may fly
+    if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(vmcnt_only(3));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (c + kNS - 1 < nch) issue(c + kNS - 1);
+    const bf16_t* A = lds + (c % kNS) * kStageElems;
+    const bf16_t* B = A + kAElems;
+    const int kvalid = j.r1 - (j.r0 + c * kKC);          // rows of this stage inside the group
 #pragma unroll
     for (int ks = 0; ks < kKC / 16; ++ks) {
       bf16x8 fa[2], fb[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int col = 16 * ks + 8 * (lane >> 5);
-        fa[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                               st + (wm + 32 * q + (lane & 31)) * kRowE + col));
-        fb[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                               st + kOpElems + (wn + 32 * q + (lane & 31)) * kRowE + col));
+        fa[q] = tr_fragment<kBM / 8>(A, wm + 32 * q, 16 * ks, lane);
+        fb[q] = tr_fragment<kBN / 8>(B, wn + 32 * q, 16 * ks, lane);
+      }
+      if (kvalid < kKC) {
+        // rows past the group's end: zero A (B holds finite repeats)
+        const int k0 = 16 * ks + 8 * (lane >> 5);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (k0 + e >= kvalid) fa[q][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0));
       }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
@@ -237,8 +284,6 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs g) {
         for (int b = 0; b < 2; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[b], fa[a], acc[a][b], 0, 0, 0);
     }
-    if (more) store_stage(lds + ((c + 1) & 1) * kStageElems);
-    __syncthreads();
   }
 
   // ---- epilogue: lane l holds output row wm + 32 a + (l % 32) and, in register
@@ -316,16 +361,16 @@ hipError_t launch_wgrad(const moe_shape& s, const bf16_t* x, const int32_t* sort
   a.F = s.F;
   a.Fs = s.Fs;
   a.S = s.T * s.k;
-  a.n_router = dwr ? (s.E + kTile - 1) / kTile * (s.D / kTile) : 0;
-  a.n_sgu = s.Fs > 0 ? (2 * s.Fs / kTile) * (s.D / kTile) : 0;
-  a.n_sd = s.Fs > 0 ? (s.D / kTile) * (s.Fs / kTile) : 0;
+  a.n_router = dwr ? (s.E + kBM - 1) / kBM * (s.D / kBN) : 0;
+  a.n_sgu = s.Fs > 0 ? (2 * s.Fs / kBM) * (s.D / kBN) : 0;
+  a.n_sd = s.Fs > 0 ? (s.D / kBM) * (s.Fs / kBN) : 0;
   const int n_long = a.n_router + a.n_sgu + a.n_sd;
   a.long_per_xcd = (n_long + kXcds - 1) / kXcds;
-  a.tiles_gu = (2 * s.F / kTile) * (s.D / kTile);
-  a.tiles_d = (s.D / kTile) * (s.F / kTile);
+  a.tiles_gu = (2 * s.F / kBM) * (s.D / kBN);
+  a.tiles_d = (s.D / kBM) * (s.F / kBN);
   a.experts_per_xcd = (s.E + kXcds - 1) / kXcds;
   const int per_xcd = a.long_per_xcd + a.experts_per_xcd * (a.tiles_gu + a.tiles_d);
-  wgrad_kernel<<<kXcds * per_xcd, 256, 0, st>>>(a);
+  wgrad_kernel<<<kXcds * per_xcd, kThreadsW, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -179,6 +179,7 @@ def test_training_entry_points_check_arguments(L):
     assert L.moe_grouped_backward_x(ctypes.byref(s16), *([p] * 6), None, *([p] * 5)) == \
         binding.MOE_ERR_INVALID_ARG
     assert b"slot_of" in L.moe_last_error()
-    wg = [p] * 16
-    wg[14] = p   # dbias requested: needs the workspace
-    assert L.moe_weight_grads(ctypes.byref(s16), *wg, None, 0, None) == binding.MOE_ERR_WORKSPACE
+    assert L.moe_weight_grads(ctypes.byref(s16), *([p] * 9), None, *([p] * 4), None, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    assert b"dw_gate_up" in L.moe_last_error()
+    assert L.moe_bias_grad(ctypes.byref(s16), p, p, None, 0, None) == binding.MOE_ERR_WORKSPACE
