@@ -207,6 +207,18 @@ def cpu_train_baseline(s, inp_host, mask, dout, target_s: float = 12.0):
             "sample": sample, "seconds": round(el, 3)}
 
 
+def copy_calibration(mib: int, dev) -> None:
+    """Three device-to-device copies of a buffer of known size (for HBM counters)."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def train_main(args):
     """One step = the training pass: masked route, permute, load statistics,
     gate/up keeping the pre-activations, down, combine; then the combine
@@ -262,6 +274,8 @@ def train_main(args):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     wg_ms = float(np.mean([a.elapsed_time(z) for a, z in evs.values()]))
+    if args.copy_mib > 0:
+        copy_calibration(args.copy_mib, dev)
 
     routed_rows = int(fb.offsets[-1].item())
     flops, nbytes = wgrad_work(s, routed_rows)
@@ -382,13 +396,7 @@ def main():
     gate_up_ms = float(np.mean([a.elapsed_time(z) for a, z in evs.values()]))
 
     if args.copy_mib > 0:
-        n = args.copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(args.copy_mib, dev)
 
     counts = b.counts.cpu().numpy()
     n_touched = int(np.count_nonzero(counts))

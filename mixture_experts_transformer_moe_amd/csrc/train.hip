@@ -125,15 +125,19 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const bf16_t* __restric
   }
 }
 
-// Block-wide sum of one value per thread (256 threads): fixed xor tree inside
-// each wave, then the 4 wave sums in order.  Every thread gets the result.
-__device__ __forceinline__ float block_sum(float v, float* red4) {
+// Block-wide sum of one value per thread (NW waves): fixed xor tree inside
+// each wave, then the wave sums in order.  Every thread gets the result.
+template <int NW = 4>
+__device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   const int wave = threadIdx.x >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red4[wave] = v;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
-  return ((red4[0] + red4[1]) + red4[2]) + red4[3];
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r += red[w];
+  return r;
 }
 
 // Combine backward, one workgroup per token: the output gradients of the
@@ -309,45 +313,57 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const float* __rest
   part[static_cast<size_t>(blockIdx.x) * E + e] = acc;
 }
 
-// sum_b part[b][e] for b = 0, 1, ..., nb - 1 in that order; the loads of 8
-// blocks are issued together ahead of their adds
-__device__ __forceinline__ float ordered_sum(const float* __restrict__ part, int nb, int E, int e) {
+// Column sums over the partial rows, 4 threads per expert (1024 threads):
+// thread (e, w) adds rows b = w, w + 4, ... in order, 8 loads in flight, and
+// the 4 sums are added in w order -- a fixed order, so the result is
+// reproducible bit for bit.
+constexpr int kFinalThreads = 1024;
+
+__device__ __forceinline__ float colsum4(const float* __restrict__ part, int nb, int E, float* red) {
+  const int e = threadIdx.x & 255, w = threadIdx.x >> 8;
   float acc = 0.f;
-  int b = 0;
-  for (; b + 8 <= nb; b += 8) {
-    float v[8];
+  if (e < E) {
+    int b = w;
+    for (; b + 28 < nb; b += 32) {
+      float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = part[static_cast<size_t>(b + u) * E + e];
+      for (int u = 0; u < 8; ++u) v[u] = part[static_cast<size_t>(b + 4 * u) * E + e];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += v[u];
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; b < nb; b += 4) acc += part[static_cast<size_t>(b) * E + e];
   }
-  for (; b < nb; ++b) acc += part[static_cast<size_t>(b) * E + e];
-  return acc;
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  return ((red[e] + red[256 + e]) + red[512 + e]) + red[768 + e];
 }
 
-__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int nb,
-                                                           int E, float* __restrict__ out) {
-  const int e = threadIdx.x;
-  if (e >= E) return;
-  out[e] = ordered_sum(part, nb, E, e);
+__global__ __launch_bounds__(kFinalThreads) void colsum_final_kernel(const float* __restrict__ part, int nb,
+                                                                     int E, float* __restrict__ out) {
+  __shared__ float red[kFinalThreads];
+  const float v = colsum4(part, nb, E, red);
+  if (threadIdx.x < E) out[threadIdx.x] = v;
 }
 
 // f, p, the auxiliary loss and its per-expert coefficients c = beta E f / N.
-__global__ __launch_bounds__(256) void load_stats_final_kernel(
+__global__ __launch_bounds__(kFinalThreads) void load_stats_final_kernel(
     const float* __restrict__ part, int nb, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ counts_global, int E, int k, float beta, float* __restrict__ f,
     float* __restrict__ p, float* __restrict__ loss, float* __restrict__ coef) {
-  __shared__ float red4[4];
+  __shared__ float red[kFinalThreads];
+  __shared__ float red16[kFinalThreads / 64];
+  constexpr int kNW = kFinalThreads / 64;
+  const float psum = colsum4(part, nb, E, red);
+  // the rest is per expert: threads 0..255, the others adding zeros
   const int e = threadIdx.x;
   const float cl = e < E ? static_cast<float>(counts[e]) : 0.f;
   const float cg = e < E ? static_cast<float>(counts_global ? counts_global[e] : counts[e]) : 0.f;
-  const float n_slots = block_sum(cl, red4);        // counts are exact in fp32 below 2^24
-  const float g_slots = block_sum(cg, red4);
+  const float n_slots = block_sum<kNW>(cl, red16);  // counts are exact in fp32 below 2^24
+  const float g_slots = block_sum<kNW>(cg, red16);
   const float N = n_slots / static_cast<float>(k);
-  const float psum = e < E ? ordered_sum(part, nb, E, e) : 0.f;
   const float pe = N > 0.f ? psum / N : 0.f;
   const float fe = g_slots > 0.f ? cg / g_slots : 0.f;
-  const float l = block_sum(fe * pe, red4);
+  const float l = block_sum<kNW>(e < E ? fe * pe : 0.f, red16);
   if (e < E) {
     f[e] = fe;
     p[e] = pe;
@@ -407,7 +423,8 @@ hipError_t launch_load_stats(const moe_shape& s, const float* logits, const int3
     colsum_partial_kernel<true><<<nb, 256, 0, st>>>(logits, topk_idx, part, s.T, s.E, s.k);
     if (hipError_t e = hipGetLastError()) return e;
   }
-  load_stats_final_kernel<<<1, 256, 0, st>>>(part, nb, counts, counts_global, s.E, s.k, beta, f, p, loss, coef);
+  load_stats_final_kernel<<<1, kFinalThreads, 0, st>>>(part, nb, counts, counts_global, s.E, s.k, beta, f, p,
+                                                      loss, coef);
   return hipGetLastError();
 }
 
@@ -418,7 +435,7 @@ hipError_t launch_colsum(const moe_shape& s, const float* m, float* out, void* w
     colsum_partial_kernel<false><<<nb, 256, 0, st>>>(m, nullptr, part, s.T, s.E, s.k);
     if (hipError_t e = hipGetLastError()) return e;
   }
-  colsum_final_kernel<<<1, 256, 0, st>>>(part, nb, s.E, out);
+  colsum_final_kernel<<<1, kFinalThreads, 0, st>>>(part, nb, s.E, out);
   return hipGetLastError();
 }
 

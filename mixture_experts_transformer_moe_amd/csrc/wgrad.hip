@@ -304,7 +304,11 @@ __global__ __launch_bounds__(kThreadsW, 2) void wgrad_kernel(WgradArgs g) {
     }
     return;
   }
+  // bf16: the tile goes through LDS (rows of 128 outputs, 16-byte units XOR-
+  // swizzled by row), then out in whole 256-byte rows, 4 rows per wave
+  // store: far fewer cache lines per store than 16-byte pieces of 32 rows
   bf16_t* out = static_cast<bf16_t*>(j.out);
+  __syncthreads();                      // every wave is done with the stages
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int m = mrow + 32 * a;
@@ -327,10 +331,21 @@ __global__ __launch_bounds__(kThreadsW, 2) void wgrad_kernel(WgradArgs g) {
           v[0][cc] = sw[0];
           v[1][cc] = sw[1];
         }
-        if (m < j.m_valid)
-          *reinterpret_cast<uint4*>(out + static_cast<size_t>(m) * j.ldo + wn + 32 * b + 16 * p + 8 * (lane >> 5)) =
-              make_uint4(v[0][0], v[0][1], v[1][0], v[1][1]);
+        const int u = (wn + 32 * b + 16 * p + 8 * (lane >> 5)) >> 3;
+        *reinterpret_cast<uint4*>(lds + m * kBN + ((u ^ (m & 15)) << 3)) =
+            make_uint4(v[0][0], v[0][1], v[1][0], v[1][1]);
       }
+  }
+  __syncthreads();
+  constexpr int kUnitsOut = kBM * kBN / 8;
+#pragma unroll
+  for (int i = 0; i < kUnitsOut / kThreadsW; ++i) {
+    const int idx = tid + kThreadsW * i;
+    const int r = idx / (kBN / 8), u = idx % (kBN / 8);
+    // non-temporal: the gradients are not read again here, and kept out of
+    // L2 they leave it to the operand rows the other tiles re-read
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * kBN + ((u ^ (r & 15)) << 3));
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + static_cast<size_t>(r) * j.ldo + 8 * u));
   }
 }
 
