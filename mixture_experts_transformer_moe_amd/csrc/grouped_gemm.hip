@@ -55,6 +55,7 @@ struct GemmArgs {
   int K, Ks;                // reduction length (routed / shared)
   int N, Ns;                // output columns (routed / shared)
   int has_shared;
+  int spread_shared;        // shared-expert tiles spread through the schedule (else last)
 };
 
 // Output side of one tile.
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     // out of the tile loop it would hold registers across the whole stream
     int lane = tid & 63;
     asm volatile("" : "+v"(lane));
-    if (MODE == kGateUp && E > 0) {
+    if (g.spread_shared && E > 0) {
       // gate_up: the shared expert's tiles (weights L2-resident after the
       // first few) are spread evenly through the schedule instead of filling
       // the last round, so that every round keeps most CUs on the HBM weight
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
             float y[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              if (MODE == kGateUp && E > 0) {
+              if constexpr (MODE == kGateUp) {
                 float gv = acc[m][j][4 * q + e], uv = acc[m][j + NB / 2][4 * q + e];
                 if constexpr (W8) {
                   gv *= wsc[j][4 * q + e];
@@ -438,6 +439,7 @@ GemmArgs gate_up_args(const moe_shape& s, const bf16_t* x_perm, const int32_t* s
   a.N = s.F;
   a.Ns = s.Fs;
   a.has_shared = s.Fs > 0;
+  a.spread_shared = 1;
   return a;
 }
 
@@ -501,6 +503,7 @@ hipError_t launch_dgrad_h_bf16(const moe_shape& s, const bf16_t* dy_perm, const 
   a.N = s.F;
   a.Ns = s.Fs;
   a.has_shared = s.Fs > 0;
+  a.spread_shared = 1;
   a.w_routed = reinterpret_cast<const unsigned char*>(wd_t);
   a.w_shared = reinterpret_cast<const unsigned char*>(wsd_t);
   return launch_tiles<kDown, false>(a, mean_rows(s), st);
@@ -524,6 +527,7 @@ hipError_t launch_dgrad_x_bf16(const moe_shape& s, const bf16_t* dgu, const int3
   a.N = s.D;
   a.Ns = s.D;
   a.has_shared = s.Fs > 0;
+  a.spread_shared = 1;
   a.w_routed = reinterpret_cast<const unsigned char*>(wgu_t);
   a.w_shared = reinterpret_cast<const unsigned char*>(wsgu_t);
   return launch_tiles<kDown, false>(a, mean_rows(s), st);

@@ -156,6 +156,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   __shared__ float w_s[kMaxK];
   __shared__ float dot_s[4][kMaxK];
   __shared__ float dsel_s[kMaxK];
+  __shared__ float z_s[kDzLd];
   __shared__ float red4[4];
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -164,6 +165,9 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     e_s[tid] = topk_idx[static_cast<size_t>(t) * k + tid];
     w_s[tid] = topk_w[static_cast<size_t>(t) * k + tid];
   }
+  // the token's logits, one per thread, loaded together
+  const float z = tid < E ? logits[static_cast<size_t>(t) * E + tid] : 0.f;
+  z_s[tid] = z;
   __syncthreads();
   const bool routed = slot_s[0] >= 0;
   if (!routed) {
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     float s[kMaxK], g[kMaxK];
     float ssum = 0.f, wg = 0.f;
     for (int j = 0; j < k; ++j) {
-      s[j] = sigmoidf(logits[static_cast<size_t>(t) * E + e_s[j]]);
+      s[j] = sigmoidf(z_s[e_s[j]]);
       g[j] = alpha * (((dot_s[0][j] + dot_s[1][j]) + dot_s[2][j]) + dot_s[3][j]);
       ssum += s[j];
       wg = fmaf(w_s[j], g[j], wg);
@@ -219,7 +223,6 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   __syncthreads();
   // logit gradient row: the auxiliary loss for every expert, plus the slots
   const int e = tid;
-  const float z = e < E ? logits[static_cast<size_t>(t) * E + e] : 0.f;
   float v = 0.f;
   if (coef != nullptr) {
     const float sg = e < E ? sigmoidf(z) : 0.f;
