@@ -55,23 +55,31 @@ WRITE_FACTOR = 1.0
 GEMM_SOURCES = ("grouped_gemm.hip", "mma_stream.h", "lds_dma.h", "moe_internal.h")
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
-    "xs2_bf16_t4096_d2048": (658145.9, 37079.5,
-                             "405c46b9f3ef5188c851e6fb8211d0f20fab3ea0cce4effaae24ae5eeac2b89d"),
+    "xs2_bf16_t4096_d2048": (663269.1, 37093.1,
+                             "476fea5d4bcd96c42681eb7341f4a2764c782ab749b1240fc48d1a95f10658b3"),
 }
 
 
-def gemm_sources_sha256() -> str:
+# The same for one launch of the weight-gradient kernel in the training pass.
+WGRAD_SOURCES = ("wgrad.hip", "lds_dma.h", "moe_internal.h")
+WGRAD_TRAFFIC = {
+    "xs2_train_bf16_t4096_d2048": (250828.6, 1581074.4,
+                                   "c1cdaa591438ced52e4dfe304fc5bd1a39ea78bcc236698343ebe2d5f88135f3"),
+}
+
+
+def sources_sha256(files=GEMM_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "mixture_experts_transformer_moe_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    rec = TRAFFIC.get(workload)
-    if rec is None or rec[2] != gemm_sources_sha256():
+def measured_traffic(workload: str, table=TRAFFIC, files=GEMM_SOURCES):
+    rec = table.get(workload)
+    if rec is None or rec[2] != sources_sha256(files):
         return None
     return (rec[0] * FETCH_FACTOR + rec[1] * WRITE_FACTOR) * 1024.0
 
@@ -281,7 +289,8 @@ def train_main(args):
     flops, nbytes = wgrad_work(s, routed_rows)
     achieved = nbytes / (wg_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(s.name, WGRAD_TRAFFIC, WGRAD_SOURCES),
             "kernel": "wgrad_kernel (moe_weight_grads)", "kernel_ms": round(wg_ms, 4),
             "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
             "mfma_tflops": round(flops / (wg_ms * 1e-3) / 1e12, 1)}
