@@ -143,8 +143,9 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // Combine backward, one workgroup per token: the output gradients of the
 // token's k expert rows (dy_perm, rows in expert order), the routing-weight
 // gradients, and the logit gradient row (fp32, and bf16 padded to 256
-// columns for the products with the router weights).  A token's slots are
-// all routed or (padding) none.
+// columns for the products with the router weights).  A padding token's
+// slots are all -1: its logit gradient is zero; a slot < 0 in a routed token
+// (not produced by the router) is left out, as if absent.
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const bf16_t* __restrict__ dout, const bf16_t* __restrict__ y_perm,
     const int32_t* __restrict__ slot_of, const int32_t* __restrict__ topk_idx,
@@ -157,6 +158,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   __shared__ float dot_s[4][kMaxK];
   __shared__ float dsel_s[kMaxK];
   __shared__ float z_s[kDzLd];
+  __shared__ int kv_s;
   __shared__ float red4[4];
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -169,7 +171,21 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   const float z = tid < E ? logits[static_cast<size_t>(t) * E + tid] : 0.f;
   z_s[tid] = z;
   __syncthreads();
-  const bool routed = slot_s[0] >= 0;
+  if (tid == 0) {
+    // keep the routed slots (slot and expert in range), in slot order
+    int kv = 0;
+    for (int j = 0; j < k; ++j) {
+      if (slot_s[j] < 0 || e_s[j] < 0 || e_s[j] >= E) continue;
+      slot_s[kv] = slot_s[j];
+      e_s[kv] = e_s[j];
+      w_s[kv] = w_s[j];
+      ++kv;
+    }
+    kv_s = kv;
+  }
+  __syncthreads();
+  const int kv = kv_s;
+  const bool routed = kv > 0;
   if (!routed) {
     for (int e = tid; e < kDzLd; e += 256) {
       if (e < E) dz[static_cast<size_t>(t) * E + e] = 0.f;
@@ -186,7 +202,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     load8(dout + static_cast<size_t>(t) * D + c, d);
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
-      if (j >= k) continue;
+      if (j >= kv) continue;
       const size_t row = static_cast<size_t>(slot_s[j]) * D + c;
       float y[8], o[8];
       load8(y_perm + row, y);
@@ -203,7 +219,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   }
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
-    if (j >= k) continue;
+    if (j >= kv) continue;
     const float v = wave_sum(part[j]);
     if (lane == 0) dot_s[wave][j] = v;
   }
@@ -212,13 +228,13 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     // renormalisation and sigmoid backward over the k slots, in slot order
     float s[kMaxK], g[kMaxK];
     float ssum = 0.f, wg = 0.f;
-    for (int j = 0; j < k; ++j) {
+    for (int j = 0; j < kv; ++j) {
       s[j] = sigmoidf(z_s[e_s[j]]);
       g[j] = alpha * (((dot_s[0][j] + dot_s[1][j]) + dot_s[2][j]) + dot_s[3][j]);
       ssum += s[j];
       wg = fmaf(w_s[j], g[j], wg);
     }
-    for (int j = 0; j < k; ++j) dsel_s[j] = (g[j] - wg) / ssum * s[j] * (1.0f - s[j]);
+    for (int j = 0; j < kv; ++j) dsel_s[j] = (g[j] - wg) / ssum * s[j] * (1.0f - s[j]);
   }
   __syncthreads();
   // logit gradient row: the auxiliary loss for every expert, plus the slots
@@ -231,7 +247,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const float cs = block_sum(ce * sg, red4);       // sum_e c_e sigma_e = Q sum_e c_e s'_e
     v = e < E ? (ce - cs / q) / q * sg * (1.0f - sg) : 0.f;
   }
-  for (int j = 0; j < k; ++j)
+  for (int j = 0; j < kv; ++j)
     if (e_s[j] == e) v += dsel_s[j];
   if (e < E) dz[static_cast<size_t>(t) * E + e] = v;
   dz16[static_cast<size_t>(t) * kDzLd + e] = e < E ? f32_to_bf16(v) : 0;

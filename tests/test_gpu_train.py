@@ -210,3 +210,42 @@ def test_xs2_training_sampled_parity():
     dzf = b.dz.cpu().numpy().astype(np.float64)
     assert_close_rel(b.dbias.cpu().numpy().astype(np.float64), dzf.sum(axis=0), 1e-5, "dbias = sum dz")
     say("xs2 training pass: sampled parity within tolerance")
+
+
+def test_two_micro_batches_share_global_counts():
+    """Global-batch statistics: each micro-batch's loss and gradients use the
+    counts summed over both micro-batches (the sum a caller forms over
+    micro-batches or ranks), and match the oracle given those counts."""
+    s = configs.variant(SMALL, name="train_micro_batch", T=200)
+    inps = [StackedInputs(LayerInputs(configs.variant(s, seed=s.seed + i))) for i in range(2)]
+    w = binding.upload_train_weights(s, inps[0].w_router, inps[0].bias, inps[0].wgu, inps[0].wd,
+                                     inps[0].shared())
+    mask = token_mask(s)
+    bufs = []
+    for i, inp in enumerate(inps):
+        say(f"micro-batch {i}: forward")
+        b = binding.alloc_train_buffers(s, torch.from_numpy(mask).cuda())
+        binding.train_forward(s, binding.to_device(inp.x, s, "cuda"), w, b, s.aux_coef)
+        bufs.append(b)
+    counts_global = bufs[0].fwd.counts + bufs[1].fwd.counts
+    dout = dout_encoded(s)
+    for i, (inp, b) in enumerate(zip(inps, bufs)):
+        say(f"micro-batch {i}: statistics and backward with the global counts")
+        c = binding.make_shape(s)
+        fb = b.fwd
+        binding.moe_load_stats(c, fb.logits, fb.topk_idx, fb.counts, counts_global, s.aux_coef, b.f, b.p,
+                               b.aux_loss, b.aux_coef, b.train_ws)
+        x = binding.to_device(inp.x, s, "cuda")
+        binding.train_backward(s, x, binding.to_device(dout, s, "cuda"), w, b)
+    torch.cuda.synchronize()
+    cg = counts_global.cpu().numpy()
+    for inp, b in zip(inps, bufs):
+        # the micro-batch's own weights are the first one's (same layer)
+        inp.wgu, inp.wd, inp._shared = inps[0].wgu, inps[0].wd, inps[0].shared()
+        inp.w_router, inp.bias = inps[0].w_router, inps[0].bias
+        r = routing_of(s, b, mask)
+        check_stats(s, b, r, s.aux_coef, cg)
+        g = TR.backward(inp, s.alpha, r, dout, s.aux_coef, cg)
+        assert_close_rel(b.dz.cpu().numpy().astype(np.float64), g.dz, TOL, "dz with global counts")
+        assert_close_rel(to_f64(b.dx), g.dx, TOL, "dx with global counts")
+        assert_close_rel(b.dw_router.cpu().numpy().astype(np.float64), g.dw_router, TOL, "dw_router")
