@@ -300,6 +300,7 @@ int moe_pack_weights_transposed(const void* w, void* w_packed, int64_t count, in
 /* Load statistics and auxiliary loss.
  *   logits, topk_idx   from moe_route_masked (topk_idx[t, 0] < 0: padding)
  *   counts [E] int32   this batch's counts (moe_permute); N = sum counts / k
+ *                      (not read when T == 0: an empty batch has N = 0, p = 0)
  *   counts_global [E] int32 or NULL: the global batch's counts (NULL = counts)
  *   beta               auxiliary-loss coefficient (not disclosed by the pages)
  *   f, p [E] fp32 out; aux_loss [1] fp32 out;

@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kFinalThreads) void colsum_final_kernel(const float
 // f, p, the auxiliary loss and its per-expert coefficients c = beta E f / N.
 __global__ __launch_bounds__(kFinalThreads) void load_stats_final_kernel(
     const float* __restrict__ part, int nb, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ counts_global, int E, int k, float beta, float* __restrict__ f,
+    const int32_t* __restrict__ counts_global, int T, int E, int k, float beta, float* __restrict__ f,
     float* __restrict__ p, float* __restrict__ loss, float* __restrict__ coef) {
   __shared__ float red[kFinalThreads];
   __shared__ float red16[kFinalThreads / 64];
@@ -375,8 +375,9 @@ __global__ __launch_bounds__(kFinalThreads) void load_stats_final_kernel(
   const float psum = colsum4(part, nb, E, red);
   // the rest is per expert: threads 0..255, the others adding zeros
   const int e = threadIdx.x;
-  const float cl = e < E ? static_cast<float>(counts[e]) : 0.f;
-  const float cg = e < E ? static_cast<float>(counts_global ? counts_global[e] : counts[e]) : 0.f;
+  // an empty batch has no routed token (its counts buffer was not written)
+  const float cl = e < E && T > 0 ? static_cast<float>(counts[e]) : 0.f;
+  const float cg = e < E ? (counts_global ? static_cast<float>(counts_global[e]) : cl) : 0.f;
   const float n_slots = block_sum<kNW>(cl, red16);  // counts are exact in fp32 below 2^24
   const float g_slots = block_sum<kNW>(cg, red16);
   const float N = n_slots / static_cast<float>(k);
@@ -442,8 +443,8 @@ hipError_t launch_load_stats(const moe_shape& s, const float* logits, const int3
     colsum_partial_kernel<true><<<nb, 256, 0, st>>>(logits, topk_idx, part, s.T, s.E, s.k);
     if (hipError_t e = hipGetLastError()) return e;
   }
-  load_stats_final_kernel<<<1, kFinalThreads, 0, st>>>(part, nb, counts, counts_global, s.E, s.k, beta, f, p,
-                                                      loss, coef);
+  load_stats_final_kernel<<<1, kFinalThreads, 0, st>>>(part, nb, counts, counts_global, s.T, s.E, s.k, beta, f,
+                                                      p, loss, coef);
   return hipGetLastError();
 }
 

@@ -249,3 +249,27 @@ def test_two_micro_batches_share_global_counts():
         assert_close_rel(b.dz.cpu().numpy().astype(np.float64), g.dz, TOL, "dz with global counts")
         assert_close_rel(to_f64(b.dx), g.dx, TOL, "dx with global counts")
         assert_close_rel(b.dw_router.cpu().numpy().astype(np.float64), g.dw_router, TOL, "dw_router")
+
+
+def test_pack_weights_transposed_layout():
+    """moe_pack_weights_transposed against the layout include/moe.h documents,
+    element by element, with the padded columns zero and nothing written past
+    the output."""
+    rng = np.random.default_rng(3)
+    count, rows, cols, kp = 2, 40, 64, 64
+    host = rng.integers(1, 1 << 15, size=(count, rows, cols), dtype=np.int64).astype(np.int16)
+    w = torch.from_numpy(host).view(torch.bfloat16).cuda()
+    n = binding.moe_packed_transposed_bytes(count, rows, cols, kp) // 2
+    big = torch.empty(n + 4096, dtype=torch.bfloat16, device="cuda")
+    big.view(torch.int16)[n:] = 0x5a5a
+    binding.moe_pack_weights_transposed(w, big[:n], count, rows, cols, kp)
+    torch.cuda.synchronize()
+    assert bool((big.view(torch.int16)[n:] == 0x5a5a).all()), "write past the packed output"
+    got = big[:n].view(torch.int16).cpu().numpy()
+    ref = np.zeros(n, dtype=np.int16)
+    for i in range(count):
+        for r in range(cols):                  # rows of the transpose
+            for c in range(kp):                # its columns: source rows, zero past `rows`
+                o = ((r // 32) * (kp // 16) + c // 16) * 512 + ((r % 32) + 32 * ((c % 16) // 8)) * 8 + c % 8
+                ref[i * cols * kp + o] = host[i, c, r] if c < rows else 0
+    assert np.array_equal(got, ref)
