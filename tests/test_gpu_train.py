@@ -273,3 +273,32 @@ def test_pack_weights_transposed_layout():
                 o = ((r // 32) * (kp // 16) + c // 16) * 512 + ((r % 32) + 32 * ((c % 16) // 8)) * 8 + c % 8
                 ref[i * cols * kp + o] = host[i, c, r] if c < rows else 0
     assert np.array_equal(got, ref)
+
+
+def test_m1_width_training_sampled_parity():
+    """The training pass at M.1's widths (D = 4096, F = Fs = 1024, 8192 tokens,
+    ~256 rows per expert: the backward GEMMs' 96-row, 4-block tiles), on
+    sampled tokens and experts."""
+    s = configs.variant(configs.M1_T8192, name="m1_train_bf16_t8192_d4096", pad_frac=1 / 16,
+                        aux_coef=1e-3)
+    inp = StackedInputs(LayerInputs(s))
+    mask, dout = token_mask(s), dout_encoded(s)
+    w, b = run_train(s, inp, mask, dout, s.aux_coef)
+    r = routing_of(s, b, mask)
+    check_stats(s, b, r, s.aux_coef)
+    rng = np.random.default_rng(1)
+    toks = sorted(set(rng.choice(s.T, 12, replace=False).tolist()) | {0, s.T - 1})
+    say(f"oracle on {len(toks)} sampled tokens")
+    dz, dx = TR.token_grads(inp, s.alpha, r, dout, toks, s.aux_coef)
+    assert_close_rel(b.dz.cpu().numpy()[toks].astype(np.float64), dz, TOL, "sampled dz")
+    assert_close_rel(to_f64(b.dx)[toks], dx, TOL, "sampled dx")
+    nz = np.nonzero(r.counts)[0]
+    for e in sorted({int(np.argmax(r.counts)), int(rng.choice(nz))}):
+        say(f"oracle on expert {e} ({int(r.counts[e])} rows)")
+        dwgu, dwd, _, _ = TR.expert_grads(inp, s.alpha, r, dout, e)
+        assert_close_rel(to_f64(b.dw_gate_up[e]), dwgu, TOL, f"dw_gate_up[{e}]")
+        assert_close_rel(to_f64(b.dw_down[e]), dwd, TOL, f"dw_down[{e}]")
+    x = O.widen(inp.x)
+    dz16 = to_f64(b.dz16)[:, :s.E]
+    assert_close_rel(b.dw_router.cpu().numpy().astype(np.float64), dz16.T @ x, 1e-3, "dw_router = dz^T x")
+    say("m1-width training pass: sampled parity within tolerance")
