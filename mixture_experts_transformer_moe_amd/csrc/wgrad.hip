@@ -23,13 +23,16 @@
 // row k0 + j / 4, columns c0 + 4 (j mod 4) .. + 3, and lane i receives rows
 // k0 .. k0 + 3 of column c0 + i; with the swizzle the 16 lanes of a read hit
 // distinct banks.  Three stages are in flight (72 KB, 2 workgroups per CU):
-// the tiles are short (an expert's ~100-200 rows are a few stages), so the
-// kernel is bound by the latency of its loads unless several stages fly at
-// once.  Rows past the group's end load its last row again and the A values
-// of the last stage's rows past the end are zeroed, so they add nothing.
+// the tiles are short (an expert's ~100-200 rows are a few stages), so
+// several stages must fly at once to cover the load latency.  Rows past the
+// group's end load its last row again and the A values of the last stage's
+// rows past the end are zeroed, so they add nothing.
 // A tile is 256 x 128 outputs, 8 waves of 64 x 64 (2 x 2 MFMA blocks); the
 // MFMA's first operand is the B fragment, so a lane holds consecutive output
-// columns and stores 16 bytes after a lane-pair swap, as in the forward GEMMs.
+// columns, 8 of them after a lane-pair swap.  The bf16 tile then goes through
+// LDS and out as whole 256-byte rows with non-temporal stores (the router's
+// fp32 rows go out directly).  The gradients written (1.6 GB at the XS.2
+// shape) dominate the traffic, with the operand rows the tiles re-read.
 // Gathered token ids (x rows of a routed expert) come through scalar loads,
 // 4 per wave and stage, so that no vector wait drains the stages in flight.
 //

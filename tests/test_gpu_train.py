@@ -140,6 +140,10 @@ EDGE = {
     "T1": dict(T=1, pad_frac=0.0),
     "E256_T70": dict(T=70, E=256, k=8, seq_len=32),
     "wide_D512_rows256": dict(T=512, D=512, E=16, k=8),
+    # experts not a multiple of the 8 XCDs' runs; the largest k; a router bias
+    "E12_k3": dict(E=12, k=3),
+    "k16_E64": dict(E=64, k=16, alpha=1.0),
+    "zipf_bias": dict(E=64, k=8, bias="zipf"),
 }
 
 
