@@ -259,7 +259,7 @@ int moe_combine(const moe_shape* shape, const void* y_perm, const void* y_shared
                 const int32_t* slot_of, const float* topk_w, void* out, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Training pass (MOE_BF16 only; MOE_ERR_UNSUPPORTED otherwise).
+ * Training pass (MOE_BF16 only, and T * 2 Fs < 2^31; MOE_ERR_UNSUPPORTED otherwise).
  *
  * Forward: moe_route_masked, moe_permute, moe_load_stats,
  * moe_grouped_gate_up_train, moe_grouped_down, moe_combine.  Backward of

@@ -376,6 +376,9 @@ namespace {
 int check_train_shape(const moe_shape* shape) {
   if (int r = check_shape(shape)) return r;
   if (shape->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the training pass is bf16 only");
+  // the shared expert's [dg | du] rows (2 Fs wide) are addressed by 32-bit byte offsets
+  if (static_cast<int64_t>(shape->T) * 2 * shape->Fs * 2 >= (int64_t{1} << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "training: T * 2 Fs must stay below 2^31");
   return MOE_OK;
 }
 

@@ -169,6 +169,9 @@ def test_training_entry_points_check_arguments(L):
     args = [p] * 11
     assert L.moe_combine_backward(ctypes.byref(s32), *args) == binding.MOE_ERR_UNSUPPORTED
     assert L.moe_grouped_gate_up_train(ctypes.byref(s32), *([p] * 9)) == binding.MOE_ERR_UNSUPPORTED
+    big = binding.make_shape(configs.variant(configs.XS2_T4096, T=600000, Fs=2048))
+    assert L.moe_combine_backward(ctypes.byref(big), *args) == binding.MOE_ERR_UNSUPPORTED
+    assert b"2 Fs" in L.moe_last_error()
     # missing pointers and workspace are caught before any launch
     assert L.moe_combine_backward(ctypes.byref(s16), None, *([p] * 10)) == binding.MOE_ERR_INVALID_ARG
     assert b"dout" in L.moe_last_error()
