@@ -55,16 +55,16 @@ WRITE_FACTOR = 1.0
 GEMM_SOURCES = ("grouped_gemm.hip", "mma_stream.h", "lds_dma.h", "moe_internal.h")
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
-    "xs2_bf16_t4096_d2048": (663269.1, 37093.1,
-                             "476fea5d4bcd96c42681eb7341f4a2764c782ab749b1240fc48d1a95f10658b3"),
+    "xs2_bf16_t4096_d2048": (662208.4, 37045.5,
+                             "d744b87270a8aa89df547df53a289687caf0be63c80322956ae13612eac667f4"),
 }
 
 
 # The same for one launch of the weight-gradient kernel in the training pass.
 WGRAD_SOURCES = ("wgrad.hip", "lds_dma.h", "moe_internal.h")
 WGRAD_TRAFFIC = {
-    "xs2_train_bf16_t4096_d2048": (250828.6, 1581074.4,
-                                   "c1cdaa591438ced52e4dfe304fc5bd1a39ea78bcc236698343ebe2d5f88135f3"),
+    "xs2_train_bf16_t4096_d2048": (250792.6, 1581082.6,
+                                   "5c7fdf03ad0afb4332146fa35647855978bae2e5cdf48d7d4282a1236283ed2b"),
 }
 
 
