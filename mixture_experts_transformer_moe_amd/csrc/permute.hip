@@ -25,6 +25,7 @@ namespace {
 
 constexpr int kTB = 256;        // tokens per block
 constexpr int kMaxE = 256;
+constexpr int kMaxK = 16;       // the router's limit on k
 static_assert(kTB == kMaxE, "the scatter kernel keeps one thread per expert");
 
 __device__ __forceinline__ int clamp_e(int e, int E) { return e >= E ? E - 1 : e; }
@@ -58,6 +59,14 @@ __global__ __launch_bounds__(kTB) void perm_scatter_kernel(const int32_t* __rest
   __shared__ int32_t base[kMaxE];
   __shared__ int32_t scan[kMaxE];
   const int e = threadIdx.x;                      // kTB == kMaxE: one thread per expert
+  const int local = threadIdx.x;                  // and one per token of the block
+  const int t = blockIdx.x * kTB + local;
+  // the token's experts, loaded first so that their latency overlaps the
+  // histogram sums and the scan
+  int ej[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    ej[j] = (t < T && j < k) ? clamp_e(idx[static_cast<size_t>(t) * k + j], E) : -1;
   for (int i = threadIdx.x; i < kMaxE * (kTB / 32); i += kTB) (&chose[0][0])[i] = 0u;
   int total = 0, before = 0;
   if (e < E) {
@@ -95,26 +104,24 @@ __global__ __launch_bounds__(kTB) void perm_scatter_kernel(const int32_t* __rest
     if (e == E - 1) offsets[E] = scan[e];
   }
   __syncthreads();
-  const int local = threadIdx.x;
-  const int t = blockIdx.x * kTB + local;
   const int word = local >> 5;
   const uint32_t bit = 1u << (local & 31);
-  if (t < T)
-    for (int j = 0; j < k; ++j) {
-      const int ej = clamp_e(idx[static_cast<size_t>(t) * k + j], E);
-      if (ej >= 0) atomicOr(&chose[ej][word], bit);
-    }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (ej[j] >= 0) atomicOr(&chose[ej[j]][word], bit);
   __syncthreads();
   if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int ej = clamp_e(idx[static_cast<size_t>(t) * k + j], E);
-      if (ej < 0) {
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) continue;
+      const int ex = ej[j];
+      if (ex < 0) {
         slot_of[static_cast<size_t>(t) * k + j] = -1;
         continue;
       }
-      int rank = __popc(chose[ej][word] & (bit - 1u));
-      for (int w = 0; w < word; ++w) rank += __popc(chose[ej][w]);
-      const int pos = base[ej] + rank;
+      int rank = __popc(chose[ex][word] & (bit - 1u));
+      for (int w = 0; w < word; ++w) rank += __popc(chose[ex][w]);
+      const int pos = base[ex] + rank;
       slot_of[static_cast<size_t>(t) * k + j] = pos;
       sorted_token[pos] = t;
     }

@@ -27,6 +27,11 @@ __device__ __forceinline__ uint32_t order_key(float z) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The value a key came from (-0.0 comes back as +0.0).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
 // Row-wide (16 lanes) reductions through DPP row shifts: after them lane 15
 // of each row holds the row's result, read back by readlane and handed to
 // every lane of the row.  `id` is the identity of the operation.
@@ -53,6 +58,7 @@ __device__ __forceinline__ float row_sum_f32(float v) {
   return __int_as_float(row == 0 ? b0 : row == 1 ? b1 : row == 2 ? b2 : b3);
 }
 
+constexpr int kXcds = 8;                       // workgroup b runs on XCD b mod 8
 constexpr int kTopkThreads = 256;              // 4 waves x 4 tokens
 constexpr int kTopkTokens = kTopkThreads / 16;
 
@@ -80,6 +86,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     if (e >= E) taken |= 1u << i;
   }
   int my_e = 0;
+  uint32_t my_key = 0;
   for (int j = 0; j < k; ++j) {
     uint32_t m = 0;
 #pragma unroll
@@ -92,10 +99,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
       if (!((taken >> i) & 1u) && key[i] == best) cand = static_cast<uint32_t>(c + 16 * i);
     const int e = static_cast<int>(row_reduce_u32(cand, 0xffffu, [](uint32_t a, uint32_t b) { return min(a, b); }));
     if ((e & 15) == c) taken |= 1u << (e >> 4);
-    if (c == j) my_e = e;
+    if (c == j) {
+      my_e = e;
+      my_key = best;
+    }
   }
-  // sigmoid of the selected logits (exact fp32 values), renormalised
-  const float s = c < k ? 1.0f / (1.0f + expf(-z[my_e])) : 0.f;
+  // sigmoid of the selected logits (the exact fp32 values, recovered from
+  // their keys), renormalised
+  const float s = c < k ? 1.0f / (1.0f + expf(-key_value(my_key))) : 0.f;
   const float sum = row_sum_f32(s);
   const bool routed = mask == nullptr || mask[t] != 0;
   if (t_raw < T && c < k) {
@@ -129,8 +140,16 @@ __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __rest
   static_assert(NS * kStageElems * 2 <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) bf16_t lds[NS * kStageElems];
   const int tiles_n = (E + TN - 1) / TN;
-  const int t0 = (blockIdx.x / tiles_n) * TM;
-  const int e0 = (blockIdx.x % tiles_n) * TN;
+  // blocks numbered token block-major and dealt to the XCDs in runs of
+  // consecutive numbers (XCD x takes the x-th run, one block per workgroup it
+  // runs), so that the blocks of one token block share an L2 and read its
+  // token rows from HBM once (dealt round-robin they were read once per
+  // expert block)
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % kXcds;
+  const int tile = xcd * (G / kXcds) + min(xcd, G % kXcds) + blockIdx.x / kXcds;
+  const int t0 = (tile / tiles_n) * TM;
+  const int e0 = (tile % tiles_n) * TN;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int ks = wave % KS;
@@ -160,7 +179,7 @@ __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __rest
   // workgroups that share router rows start at different K offsets, so that
   // they do not all ask the same L2 lines for the same block at once (each
   // token's sum is still taken in one fixed order)
-  const int rot = (blockIdx.x / tiles_n) % nst;
+  const int rot = (tile / tiles_n) % nst;
   auto issue = [&](int slot, int s) {
     const uint32_t base = lds0 + static_cast<uint32_t>(slot * kStageElems * 2);
     const int sr = s + rot < nst ? s + rot : s + rot - nst;
@@ -260,10 +279,13 @@ hipError_t launch_route_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* 
                              const float* bias, const uint8_t* mask, float* logits, int32_t* idx,
                              float* w, hipStream_t st) {
   // 64 x 64 blocks when they are enough to fill the chip, else 32 x 32 blocks
-  // with the K split over the workgroup's waves
+  // with the K split over the workgroup's waves.  The stages are few: the
+  // loads in flight per CU do not grow past a few stages' worth, and every
+  // stage beyond that adds clamped repeat loads at the end of the K loop
+  // (measured: 4 stages 11 to 16% faster than 8 on 8192 and 32768 tokens)
   const int big = ((s.T + 63) / 64) * ((s.E + 63) / 64);
   if (big >= 128) {
-    route_bf16_kernel<64, 64, 1, 8><<<big, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
+    route_bf16_kernel<64, 64, 1, 4><<<big, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
   } else {
     const int blocks = ((s.T + 31) / 32) * ((s.E + 31) / 32);
     route_bf16_kernel<32, 32, 4, 4><<<blocks, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
