@@ -10,9 +10,10 @@
 //           the candidates e = c + 16 i.  Each of the k rounds takes the
 //           largest key among the candidates not yet taken (row maximum over
 //           an order-preserving uint32 image of z), then the lowest index
-//           holding it (row minimum), so the order is (z descending, index
-//           ascending) exactly and independent of timing.  Sigmoid of the
-//           selected logits, renormalised over the k slots.
+//           holding it (row minimum), and zeroes that candidate's key, so the
+//           order is (z descending, index ascending) exactly and independent
+//           of timing.  Sigmoid of the selected logits, renormalised over the
+//           k slots.
 #include "lds_dma.h"
 
 namespace moe {
@@ -32,21 +33,20 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-// Row-wide (16 lanes) reductions through DPP row shifts: after them lane 15
-// of each row holds the row's result, read back by readlane and handed to
-// every lane of the row.  `id` is the identity of the operation.
+// Row-wide (16 lanes) reduction of an associative, commutative operation
+// through DPP row rotations: after rotating by 1, 2, 4 and 8 lanes every lane
+// of the row holds the result.
 template <typename Op>
-__device__ __forceinline__ uint32_t row_reduce_u32(uint32_t v, uint32_t id, Op op) {
-  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(v), 0x111, 0xf, 0xf, false)));
-  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(v), 0x112, 0xf, 0xf, false)));
-  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(v), 0x114, 0xf, 0xf, false)));
-  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(v), 0x118, 0xf, 0xf, false)));
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
-  const int row = (threadIdx.x & 63) >> 4;
-  return row == 0 ? r0 : row == 1 ? r1 : row == 2 ? r2 : r3;
+__device__ __forceinline__ uint32_t row_allreduce_u32(uint32_t v, Op op) {
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x121, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x122, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xf, 0xf, false)));
+  return v;
 }
 
+// Row sum: lane 15 of each row after DPP row shifts, read back by readlane and
+// handed to every lane of the row (one summation order for the whole row).
 __device__ __forceinline__ float row_sum_f32(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
@@ -72,33 +72,34 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   const int t_raw = blockIdx.x * kTopkTokens + (threadIdx.x >> 4);
   const int t = min(t_raw, T - 1);                 // rows past T compute a copy of the last one
   const float* z = logits + static_cast<size_t>(t) * E;
+  // keys of the candidates still in the running; 0 marks one taken or absent
+  // (real keys are >= 1)
   uint32_t key[16];
-  uint32_t taken = 0;                              // bit i: candidate c + 16 i taken or absent
   // all 16 loads unconditional (clamped index), so that they are in flight
   // together
   float zv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) zv[i] = z[min(c + 16 * i, E - 1)];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = c + 16 * i;
-    key[i] = e < E ? order_key(zv[i]) : 0u;        // real keys are >= 1
-    if (e >= E) taken |= 1u << i;
-  }
+  for (int i = 0; i < 16; ++i) key[i] = order_key(zv[i]) & (c + 16 * i < E ? ~0u : 0u);
   int my_e = 0;
   uint32_t my_key = 0;
   for (int j = 0; j < k; ++j) {
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (!((taken >> i) & 1u)) m = max(m, key[i]);
-    const uint32_t best = row_reduce_u32(m, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+    for (int i = 0; i < 16; ++i) m = max(m, key[i]);
+    const uint32_t best = row_allreduce_u32(m, [](uint32_t a, uint32_t b) { return max(a, b); });
+    // the lowest index holding the best key
     uint32_t cand = 0xffffu;
 #pragma unroll
     for (int i = 15; i >= 0; --i)
-      if (!((taken >> i) & 1u) && key[i] == best) cand = static_cast<uint32_t>(c + 16 * i);
-    const int e = static_cast<int>(row_reduce_u32(cand, 0xffffu, [](uint32_t a, uint32_t b) { return min(a, b); }));
-    if ((e & 15) == c) taken |= 1u << (e >> 4);
+      if (key[i] == best) cand = static_cast<uint32_t>(c + 16 * i);
+    const int e = static_cast<int>(row_allreduce_u32(cand, [](uint32_t a, uint32_t b) { return min(a, b); }));
+    // taken: key zeroed in the lane that holds it
+    const int taken_i = (e & 15) == c ? e >> 4 : 16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (taken_i == i) key[i] = 0u;
     if (c == j) {
       my_e = e;
       my_key = best;
