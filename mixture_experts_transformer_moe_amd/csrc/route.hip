@@ -14,6 +14,8 @@
 //           order is (z descending, index ascending) exactly and independent
 //           of timing.  Sigmoid of the selected logits, renormalised over the
 //           k slots.
+#include <type_traits>
+
 #include "lds_dma.h"
 
 namespace moe {
@@ -118,26 +120,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 
 // Router logits, bf16: a workgroup of 4 waves computes a TM x TN block of
 // logits (tokens x experts) over the whole of D.  Wave w sits at (tm, tn, ks):
-// it owns the 32 x 32 block (tm, tn) and, when the four waves split K (KS = 4
+// it owns the MF x MF block (tm, tn) and, when the four waves split K (KS = 4
 // for small batches, so that few tokens still keep 4 load streams per CU),
 // the K blocks ks, ks + KS, ...; the partial blocks are summed in LDS in ks
 // order.  Token rows and router rows reach LDS by direct global->LDS loads
 // (each covers 8 rows x 128 bytes, XOR-swizzled) through a ring of NS stages
 // of KS 64-wide K blocks, the same number of loads per wave in every stage, so
-// every wait is a constant.  v_mfma_f32_32x32x16_bf16 with the router rows as the first
-// operand: lane l holds token (l mod 32), register quads 4 adjacent experts.
+// every wait is a constant.  MFMA with the router rows as the first operand:
+// 32 x 32 blocks (v_mfma_f32_32x32x16_bf16): lane l holds token (l mod 32),
+// register quads 4 adjacent experts; 16 x 16 blocks (TM = TN = 16, for the
+// smallest batches: 4 times the workgroups, each reading half the rows;
+// v_mfma_f32_16x16x32_bf16): lane l holds token (l mod 16) and experts
+// 4 (l / 16) + 0..3.
 template <int TM, int TN, int KS, int NS>
 __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __restrict__ x,
                                                             const bf16_t* __restrict__ wr,
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ logits, int T, int D,
                                                             int E) {
+  constexpr int MF = TM < 32 ? 16 : 32;                // MFMA block edge
   constexpr int kRows = TM + TN;                       // rows per K block: tokens, then experts
   constexpr int kBlockElems = kRows * kPipeBK;
   constexpr int kStageElems = KS * kBlockElems;
   constexpr int kLoads = KS * kRows / 8;               // 1 KB loads per stage
   constexpr int LPW = kLoads / 4;                      // per wave
-  static_assert((TM / 32) * (TN / 32) * KS == 4 && kLoads % 4 == 0, "4 waves, equal loads per stage");
+  static_assert((TM / MF) * (TN / MF) * KS == 4 && kLoads % 4 == 0, "4 waves, equal loads per stage");
+  static_assert(MF == 32 || (TM == 16 && TN == 16), "16 x 16 blocks: one per wave");
   static_assert(NS * kStageElems * 2 <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) bf16_t lds[NS * kStageElems];
   const int tiles_n = (E + TN - 1) / TN;
@@ -154,8 +162,8 @@ __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __rest
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int ks = wave % KS;
-  const int tm = (wave / KS) % (TM / 32);
-  const int tn = (wave / KS) / (TM / 32);
+  const int tm = (wave / KS) % (TM / MF);
+  const int tn = (wave / KS) / (TM / MF);
   const int NKB = D / kPipeBK;                         // a multiple of KS
 
   // this lane's LPW loads per stage: load q of wave w is load i = LPW w + q of
@@ -191,9 +199,11 @@ __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __rest
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s, min(s, nst - 1));
 
-  f32x16 acc = f32x16{0.f};
-  const int arow = 32 * tm + (lane & 31);
-  const int brow = TM + 32 * tn + (lane & 31);
+  using Acc = std::conditional_t<MF == 32, f32x16, f32x4>;
+  constexpr int NR = MF == 32 ? 16 : 4;                // accumulator registers
+  Acc acc = Acc{0.f};
+  const int arow = MF * tm + (lane & (MF - 1));
+  const int brow = TM + MF * tn + (lane & (MF - 1));
   int slot = 0;
   for (int s = 0; s < nst; ++s) {
     // this stage was issued NS - 1 stages ago; the NS - 2 later ones (LPW
@@ -202,17 +212,23 @@ __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __rest
     __builtin_amdgcn_s_barrier();
     issue(slot == 0 ? NS - 1 : slot - 1, min(s + NS - 1, nst - 1));
     const bf16_t* blk = lds + slot * kStageElems + ks * kBlockElems;
-    // all fragments of the block first: one LDS latency per block, not per step
-    bf16x8 fa[4], fb[4];
+    // all fragments of the block first: one LDS latency per block, not per
+    // step.  A step covers 16 (32 x 32 blocks) or 32 (16 x 16) of the 64 K
+    // values; lane l takes 16-byte chunk l / MF of the step's chunks.
+    constexpr int kSteps = MF == 32 ? 4 : 2;
+    bf16x8 fa[kSteps], fb[kSteps];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = 2 * i + (lane >> 5);
+    for (int i = 0; i < kSteps; ++i) {
+      const int ch = (8 / kSteps) * i + lane / MF;
       fb[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&blk[pipe_swz(brow, ch)]));
       fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&blk[pipe_swz(arow, ch)]));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[i], acc, 0, 0, 0);
+    for (int i = 0; i < kSteps; ++i) {
+      if constexpr (MF == 32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[i], acc, 0, 0, 0);
+      else acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[i], fa[i], acc, 0, 0, 0);
+    }
     slot = slot + 1 == NS ? 0 : slot + 1;
   }
   // the tail loads (clamped repeats) land before LDS is reused or the
@@ -220,24 +236,25 @@ __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __rest
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   if constexpr (KS > 1) {
     __builtin_amdgcn_s_barrier();
-    float* red = reinterpret_cast<float*>(lds);        // [KS][16][64]
+    float* red = reinterpret_cast<float*>(lds);        // [KS][NR][64]
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[(ks * 16 + r) * 64 + lane] = acc[r];
+    for (int r = 0; r < NR; ++r) red[(ks * NR + r) * 64 + lane] = acc[r];
     __syncthreads();
     if (ks != 0) return;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < NR; ++r) {
       float v = red[r * 64 + lane];
 #pragma unroll
-      for (int j = 1; j < KS; ++j) v += red[(j * 16 + r) * 64 + lane];
+      for (int j = 1; j < KS; ++j) v += red[(j * NR + r) * 64 + lane];
       acc[r] = v;
     }
   }
-  const int t = t0 + 32 * tm + (lane & 31);
+  const int t = t0 + MF * tm + (lane & (MF - 1));
   if (t >= T) return;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = e0 + 32 * tn + mfma32_row(4 * q, lane);   // 4 adjacent experts
+  for (int q = 0; q < NR / 4; ++q) {
+    // 4 adjacent experts
+    const int e = e0 + MF * tn + (MF == 32 ? mfma32_row(4 * q, lane) : 4 * (lane >> 4));
     float z[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) z[c] = acc[4 * q + c] + ((bias && e + c < E) ? bias[min(e + c, E - 1)] : 0.f);
@@ -280,16 +297,20 @@ hipError_t launch_route_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* 
                              const float* bias, const uint8_t* mask, float* logits, int32_t* idx,
                              float* w, hipStream_t st) {
   // 64 x 64 blocks when they are enough to fill the chip, else 32 x 32 blocks
-  // with the K split over the workgroup's waves.  The stages are few: the
+  // with the K split over the workgroup's waves, else (fewer than half as many
+  // as there are CUs) 16 x 16 blocks.  The stages are few: the
   // loads in flight per CU do not grow past a few stages' worth, and every
   // stage beyond that adds clamped repeat loads at the end of the K loop
   // (measured: 4 stages 11 to 16% faster than 8 on 8192 and 32768 tokens)
   const int big = ((s.T + 63) / 64) * ((s.E + 63) / 64);
+  const int mid = ((s.T + 31) / 32) * ((s.E + 31) / 32);
   if (big >= 128) {
     route_bf16_kernel<64, 64, 1, 4><<<big, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
+  } else if (mid >= 128) {
+    route_bf16_kernel<32, 32, 4, 4><<<mid, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
   } else {
-    const int blocks = ((s.T + 31) / 32) * ((s.E + 31) / 32);
-    route_bf16_kernel<32, 32, 4, 4><<<blocks, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
+    const int blocks = ((s.T + 15) / 16) * ((s.E + 15) / 16);
+    route_bf16_kernel<16, 16, 4, 4><<<blocks, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
   }
   if (hipError_t e = hipGetLastError()) return e;
   return launch_topk(s, logits, mask, idx, w, st);
