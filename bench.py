@@ -320,6 +320,9 @@ def main():
     # the clocks take some tens of milliseconds of load to settle
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=configs.BENCH_WORKLOAD, choices=sorted(configs.WORKLOADS))
+    ap.add_argument("--split-shared", action="store_true",
+                    help="run the shared expert on a second stream beside the router and the "
+                         "permutation (moe_shared_ffn), the grouped GEMMs over the routed experts only")
     ap.add_argument("--x-perm", action="store_true",
                     help="materialise x_perm in moe_permute and read it in the first GEMM "
                          "(default: the first GEMM gathers token rows through sorted_token)")
@@ -364,7 +367,20 @@ def main():
     c = binding.make_shape(s)
     stream = torch.cuda.current_stream(dev)
 
+    split = args.split_shared and not w.fp8 and s.Fs > 0 and s.dtype == "bf16"
+    if split:
+        side = torch.cuda.Stream(device=dev)
+        ev_shared, ev_done = torch.cuda.Event(), torch.cuda.Event()
+        ev_done.record(stream)
+        h_shared = b.h[s.T * s.k * s.F:]
+
     def step(ev=None):
+        if split:
+            # the shared expert on a second stream, beside the router and the
+            # permutation; it rewrites y_shared once the previous combine is done
+            side.wait_event(ev_done)
+            binding.moe_shared_ffn(c, x, w.ws_gate_up, w.ws_down, h_shared, b.y_shared, side)
+            ev_shared.record(side)
         binding.moe_route(c, x, w.w_router, w.bias, b.logits, b.topk_idx, b.topk_w, stream)
         binding.moe_permute(c, b.topk_idx, x, b.counts, b.offsets, b.sorted_token, b.slot_of,
                             b.x_perm, b.workspace, stream)
@@ -376,16 +392,20 @@ def main():
                                             b.h, stream)
         else:
             binding.moe_grouped_gate_up(c, b.x_perm, b.sorted_token, x, b.offsets, w.w_gate_up,
-                                        w.ws_gate_up, b.h, stream)
+                                        None if split else w.ws_gate_up, b.h, stream)
         if ev is not None:
             ev[1].record(stream)
         if w.fp8:
             binding.moe_grouped_down_fp8(c, b.h, b.offsets, w.w_down, w.w_down_scale, w.ws_down,
                                          w.ws_down_scale, b.y_perm, b.y_shared, stream)
         else:
-            binding.moe_grouped_down(c, b.h, b.offsets, w.w_down, w.ws_down, b.y_perm, b.y_shared,
-                                     stream)
+            binding.moe_grouped_down(c, b.h, b.offsets, w.w_down, None if split else w.ws_down,
+                                     b.y_perm, b.y_shared, stream)
+        if split:
+            stream.wait_event(ev_shared)
         binding.moe_combine(c, b.y_perm, b.y_shared, b.slot_of, b.topk_w, b.out, stream)
+        if split:
+            ev_done.record(stream)
 
     for _ in range(args.warmup):
         step()

@@ -169,7 +169,9 @@ size_t moe_packed_bytes(int64_t count, int32_t rows, int32_t cols, int32_t dtype
  *   w_gate_up    E matrices [2F, D] elem, packed (moe_pack_weights, count E):
  *                rows 0..F-1 = gate projection, F..2F-1 = up projection
  *   ws_gate_up   one matrix [2Fs, D] elem, packed, same split; ignored (may be
- *                NULL) when Fs == 0
+ *                NULL) when Fs == 0.  bf16: NULL with Fs > 0 computes the routed
+ *                experts only and leaves the shared rows of h untouched (the
+ *                shared expert then runs through moe_shared_ffn)
  *   h            [k*T*F + T*Fs] elem out: routed rows [k*T, F], then shared rows [T, Fs]
  * The h values are rounded once to elem (bf16 round-to-nearest-even). */
 int moe_grouped_gate_up(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
@@ -181,12 +183,30 @@ int moe_grouped_gate_up(const moe_shape* shape, const void* x_perm, const int32_
  *   h         as written by moe_grouped_gate_up
  *   offsets   [E+1] int32
  *   w_down    E matrices [D, F] elem, packed (moe_pack_weights, count E)
- *   ws_down   one matrix [D, Fs] elem, packed (ignored, may be NULL, when Fs == 0)
+ *   ws_down   one matrix [D, Fs] elem, packed (ignored, may be NULL, when Fs == 0;
+ *             bf16: NULL with Fs > 0 computes the routed experts only)
  *   y_perm    [k*T, D] elem out
- *   y_shared  [T, D] elem out (untouched when Fs == 0; may then be NULL) */
+ *   y_shared  [T, D] elem out (untouched when Fs == 0 or ws_down is NULL; may
+ *             then be NULL) */
 int moe_grouped_down(const moe_shape* shape, const void* h, const int32_t* offsets,
                      const void* w_down, const void* ws_down, void* y_perm, void* y_shared,
                      void* stream);
+
+/* The shared expert alone ("Laguna M.1/XS.2 Technical Report", Key claims: one
+ * always-on shared expert; "Laguna-M.1-base", Feed-forward: SwiGLU), bf16 only:
+ *   hs[t] = silu(Wsg x_t) * (Wsu x_t),  y_shared[t] = Wsd hs[t]  for all T tokens.
+ * It reads no routing result, so it can run on a second stream while the
+ * router and the permutation run, beside moe_grouped_gate_up and
+ * moe_grouped_down called with NULL shared weights (routed experts only).
+ *   x           [T, D] bf16
+ *   ws_gate_up  [2Fs, D] bf16 packed; ws_down [D, Fs] bf16 packed
+ *   h_shared    [T, Fs] bf16 out (h + k*T*F in the layout of moe_grouped_gate_up)
+ *   y_shared    [T, D] bf16 out
+ * Results equal those of the shared rows of moe_grouped_gate_up and
+ * moe_grouped_down bit for bit.  MOE_ERR_UNSUPPORTED for fp32, MOE_ERR_INVALID_ARG
+ * when Fs == 0. */
+int moe_shared_ffn(const moe_shape* shape, const void* x, const void* ws_gate_up,
+                   const void* ws_down, void* h_shared, void* y_shared, void* stream);
 
 /* moe_grouped_gate_up followed by moe_grouped_down on the same stream. */
 int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,

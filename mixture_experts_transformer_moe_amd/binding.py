@@ -31,7 +31,7 @@ EXPORTS = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_
            "moe_route_masked", "moe_train_workspace_bytes", "moe_packed_transposed_bytes",
            "moe_pack_weights_transposed", "moe_load_stats", "moe_grouped_gate_up_train",
            "moe_combine_backward", "moe_grouped_backward_h", "moe_grouped_backward_x",
-           "moe_weight_grads", "moe_bias_grad")
+           "moe_weight_grads", "moe_bias_grad", "moe_shared_ffn")
 
 
 class moe_shape(ctypes.Structure):
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_gate_up.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_grouped_down.restype = ctypes.c_int
         L.moe_grouped_down.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_shared_ffn.restype = ctypes.c_int
+        L.moe_shared_ffn.argtypes = [_SP, _P, _P, _P, _P, _P, _P]
         L.moe_grouped_ffn.restype = ctypes.c_int
         L.moe_grouped_ffn.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_fp8_packed_bytes.restype = ctypes.c_size_t
@@ -203,6 +205,11 @@ def moe_grouped_down(shape, h, offsets, w_down, ws_down, y_perm, y_shared, strea
     _check(lib().moe_grouped_down(ctypes.byref(shape), _ptr(h), _ptr(offsets), _ptr(w_down),
                                   _ptr(ws_down), _ptr(y_perm), _ptr(y_shared), _stream(stream)),
            "moe_grouped_down")
+
+
+def moe_shared_ffn(shape, x, ws_gate_up, ws_down, h_shared, y_shared, stream=None):
+    _check(lib().moe_shared_ffn(ctypes.byref(shape), _ptr(x), _ptr(ws_gate_up), _ptr(ws_down),
+                                _ptr(h_shared), _ptr(y_shared), _stream(stream)), "moe_shared_ffn")
 
 
 def moe_grouped_ffn(shape, x_perm, sorted_token, x, offsets, w_gate_up, w_down, ws_gate_up, ws_down,

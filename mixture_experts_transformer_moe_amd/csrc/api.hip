@@ -160,7 +160,7 @@ int moe_grouped_gate_up(const moe_shape* shape, const void* x_perm, const int32_
   NEED_PTR(x);
   NEED_PTR(offsets);
   NEED_PTR(w_gate_up);
-  if (shape->Fs > 0) NEED_PTR(ws_gate_up);
+  if (shape->Fs > 0 && shape->dtype != MOE_BF16) NEED_PTR(ws_gate_up);
   NEED_PTR(h);
   const moe_shape& s = *shape;
   if (s.dtype == MOE_BF16)
@@ -184,7 +184,7 @@ int moe_grouped_down(const moe_shape* shape, const void* h, const int32_t* offse
   NEED_PTR(offsets);
   NEED_PTR(w_down);
   NEED_PTR(y_perm);
-  if (shape->Fs > 0) {
+  if (shape->Fs > 0 && (shape->dtype != MOE_BF16 || ws_down != nullptr)) {
     NEED_PTR(ws_down);
     NEED_PTR(y_shared);
   }
@@ -199,6 +199,23 @@ int moe_grouped_down(const moe_shape* shape, const void* h, const int32_t* offse
                                        static_cast<const float*>(ws_down),
                                        static_cast<float*>(y_perm), static_cast<float*>(y_shared),
                                        as_stream(stream)));
+}
+
+int moe_shared_ffn(const moe_shape* shape, const void* x, const void* ws_gate_up,
+                   const void* ws_down, void* h_shared, void* y_shared, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (shape->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "moe_shared_ffn: bf16 only");
+  if (shape->Fs == 0) return fail(MOE_ERR_INVALID_ARG, "moe_shared_ffn: no shared expert (Fs = 0)");
+  if (shape->T == 0) return ok();
+  NEED_PTR(x);
+  NEED_PTR(ws_gate_up);
+  NEED_PTR(ws_down);
+  NEED_PTR(h_shared);
+  NEED_PTR(y_shared);
+  return launched(moe::launch_shared_ffn_bf16(
+      *shape, static_cast<const moe::bf16_t*>(x), static_cast<const moe::bf16_t*>(ws_gate_up),
+      static_cast<const moe::bf16_t*>(ws_down), static_cast<moe::bf16_t*>(h_shared),
+      static_cast<moe::bf16_t*>(y_shared), as_stream(stream)));
 }
 
 int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,

@@ -578,6 +578,7 @@ hipError_t launch_gate_up_bf16(const moe_shape& s, const bf16_t* x_perm,
   GemmArgs a = gate_up_args(s, x_perm, sorted_token, x, offsets, h);
   a.w_routed = reinterpret_cast<const unsigned char*>(wgu);
   a.w_shared = reinterpret_cast<const unsigned char*>(wsgu);
+  a.has_shared = a.has_shared && wsgu != nullptr;     // no shared weights: routed experts only
   return launch_tiles<kGateUp, false>(a, mean_rows(s), st);
 }
 
@@ -587,7 +588,31 @@ hipError_t launch_down_bf16(const moe_shape& s, const bf16_t* h, const int32_t* 
   GemmArgs a = down_args(s, h, offsets, y_perm, y_shared);
   a.w_routed = reinterpret_cast<const unsigned char*>(wd);
   a.w_shared = reinterpret_cast<const unsigned char*>(wsd);
+  a.has_shared = a.has_shared && wsd != nullptr;      // no shared weights: routed experts only
   return launch_tiles<kDown, false>(a, mean_rows(s), st);
+}
+
+hipError_t launch_shared_ffn_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* wsgu,
+                                  const bf16_t* wsd, bf16_t* hs, bf16_t* ys, hipStream_t st) {
+  // the shared expert alone: both GEMMs with the shared group only (E = 0)
+  GemmArgs a{};
+  a.a_shared = x;
+  a.w_shared = reinterpret_cast<const unsigned char*>(wsgu);
+  a.out_shared = hs;
+  a.T = s.T;
+  a.Ks = s.D;
+  a.Ns = s.Fs;
+  a.has_shared = 1;
+  if (hipError_t e = launch_tiles<kGateUp, false>(a, s.T, st)) return e;
+  GemmArgs b{};
+  b.a_shared = hs;
+  b.w_shared = reinterpret_cast<const unsigned char*>(wsd);
+  b.out_shared = ys;
+  b.T = s.T;
+  b.Ks = s.Fs;
+  b.Ns = s.D;
+  b.has_shared = 1;
+  return launch_tiles<kDown, false>(b, s.T, st);
 }
 
 hipError_t launch_gate_up_fp8(const moe_shape& s, const bf16_t* x_perm, const int32_t* sorted_token,

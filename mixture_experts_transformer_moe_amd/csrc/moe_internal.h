@@ -56,6 +56,8 @@ hipError_t launch_gate_up_bf16(const moe_shape& s, const bf16_t* x_perm,
 hipError_t launch_down_bf16(const moe_shape& s, const bf16_t* h, const int32_t* offsets,
                             const bf16_t* wd, const bf16_t* wsd, bf16_t* y_perm,
                             bf16_t* y_shared, hipStream_t st);
+hipError_t launch_shared_ffn_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* wsgu,
+                                  const bf16_t* wsd, bf16_t* hs, bf16_t* ys, hipStream_t st);
 // training pass (grouped_gemm.hip): pre-activations [g | u] of every routed
 // row and of the shared expert; dh = dy W_d; da = [dg | du] [W_g; W_u]; a
 // dense product out = a W^T with W packed [N, K]

@@ -186,3 +186,20 @@ def test_training_entry_points_check_arguments(L):
         binding.MOE_ERR_INVALID_ARG
     assert b"dw_gate_up" in L.moe_last_error()
     assert L.moe_bias_grad(ctypes.byref(s16), p, p, None, 0, None) == binding.MOE_ERR_WORKSPACE
+
+
+def test_shared_ffn_argument_checks(L):
+    p = ctypes.c_void_p(4096)
+    s = _shape()
+    assert L.moe_shared_ffn(ctypes.byref(s), None, p, p, p, p, None) == binding.MOE_ERR_INVALID_ARG
+    assert b"x is NULL" in L.moe_last_error()
+    assert L.moe_shared_ffn(ctypes.byref(_shape(Fs=0)), p, p, p, p, p, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    assert L.moe_shared_ffn(ctypes.byref(_shape(dtype="f32")), p, p, p, p, p, None) == \
+        binding.MOE_ERR_UNSUPPORTED
+    assert L.moe_shared_ffn(ctypes.byref(_shape(T=0)), None, None, None, None, None, None) == \
+        binding.MOE_OK
+    # fp32 grouped GEMMs still need the shared expert's weights
+    f32 = _shape(dtype="f32")
+    assert L.moe_grouped_down(ctypes.byref(f32), p, p, p, None, p, p, None) == \
+        binding.MOE_ERR_INVALID_ARG

@@ -193,6 +193,42 @@ def test_determinism_and_no_out_of_bounds_writes(fp8):
         assert all(torch.equal(p, q) for p, q in zip(o, outs[0]))
 
 
+@pytest.mark.parametrize("name", ["small_ragged", "xs2"])
+def test_shared_expert_on_its_own_stream_matches_the_fused_path(name):
+    """moe_shared_ffn on a second stream beside the router, the permutation and
+    the routed-only grouped GEMMs gives the fused path's results bit for bit."""
+    s = SMALL_BF16 if name == "small_ragged" else configs.XS2_T4096
+    say(f"shared expert split {s.name}")
+    inp = StackedInputs(LayerInputs(s))
+    from tests.gpu_common import upload_stacked
+    x, w = upload_stacked(inp)
+    fused = binding.alloc_buffers(s)
+    binding.layer_forward(s, x, w, fused)
+    torch.cuda.synchronize()
+    b = binding.alloc_buffers(s)
+    c = binding.make_shape(s)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(main)
+    binding.moe_shared_ffn(c, x, w.ws_gate_up, w.ws_down, b.h[s.T * s.k * s.F:], b.y_shared, side)
+    done = torch.cuda.Event()
+    done.record(side)
+    binding.moe_route(c, x, w.w_router, w.bias, b.logits, b.topk_idx, b.topk_w, main)
+    binding.moe_permute(c, b.topk_idx, x, b.counts, b.offsets, b.sorted_token, b.slot_of, b.x_perm,
+                        b.workspace, main)
+    binding.moe_grouped_gate_up(c, b.x_perm, b.sorted_token, x, b.offsets, w.w_gate_up, None, b.h,
+                                main)
+    binding.moe_grouped_down(c, b.h, b.offsets, w.w_down, None, b.y_perm, None, main)
+    main.wait_event(done)
+    binding.moe_combine(c, b.y_perm, b.y_shared, b.slot_of, b.topk_w, b.out, main)
+    torch.cuda.synchronize()
+    n = s.T * s.k
+    assert torch.equal(b.out, fused.out)
+    assert torch.equal(b.y_shared, fused.y_shared)
+    assert torch.equal(b.h, fused.h)
+    assert torch.equal(b.y_perm[:n], fused.y_perm[:n])
+
+
 def test_empty_batch_is_a_no_op():
     s = configs.variant(SMALL_BF16, T=0)
     c = binding.make_shape(s)
