@@ -55,16 +55,16 @@ WRITE_FACTOR = 1.0
 GEMM_SOURCES = ("grouped_gemm.hip", "mma_stream.h", "lds_dma.h", "moe_internal.h")
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
-    "xs2_bf16_t4096_d2048": (662208.4, 37045.5,
-                             "d744b87270a8aa89df547df53a289687caf0be63c80322956ae13612eac667f4"),
+    "xs2_bf16_t4096_d2048": (663236.4, 37040.4,
+                             "45cf557f44914b82175ec326ecca5e4ebdc36c2c4b79d39d8b25e2746143d312"),
 }
 
 
 # The same for one launch of the weight-gradient kernel in the training pass.
 WGRAD_SOURCES = ("wgrad.hip", "lds_dma.h", "moe_internal.h")
 WGRAD_TRAFFIC = {
-    "xs2_train_bf16_t4096_d2048": (250792.6, 1581082.6,
-                                   "5c7fdf03ad0afb4332146fa35647855978bae2e5cdf48d7d4282a1236283ed2b"),
+    "xs2_train_bf16_t4096_d2048": (250793.9, 1581063.6,
+                                   "ec40073f6eb5ff1c325864b70a7ecb9ecbf6943d6d6224261cb66c932b35412f"),
 }
 
 

@@ -104,14 +104,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       row_base[tid] = lo;
       cnt = ((hi - lo) + BM - 1) / BM * nt_r;
     }
+    // inclusive scan: within each wave by lane shuffles, then the totals of
+    // the waves before (two barriers instead of one pair per doubling step)
+    const int ln = tid & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(cnt, d);
+      if (ln >= d) cnt += v;
+    }
+    if (ln == 63) tile_end[tid] = cnt;                 // the wave's total, at its last entry
+    __syncthreads();
+    for (int w = 0; w < (tid >> 6); ++w) cnt += tile_end[64 * w + 63];
+    __syncthreads();
     tile_end[tid] = cnt;
     __syncthreads();
-    for (int off = 1; off < kMaxE; off <<= 1) {
-      const int v = tid >= off ? tile_end[tid - off] : 0;
-      __syncthreads();
-      tile_end[tid] += v;
-      __syncthreads();
-    }
     if (tid == 0) {
       const int routed_total = E > 0 ? tile_end[E - 1] : 0;
       // Shared-expert row-block height: the tiles run in rounds of G (one per
