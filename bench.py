@@ -84,14 +84,18 @@ def measured_traffic(workload: str, table=TRAFFIC, files=GEMM_SOURCES):
     return (rec[0] * FETCH_FACTOR + rec[1] * WRITE_FACTOR) * 1024.0
 
 
-def gate_up_work(s: configs.MoEShape, n_touched: int, fp8: bool = False):
+def gate_up_work(s: configs.MoEShape, n_touched: int, fp8: bool = False, shared: bool = True):
     """Algorithmic FLOPs and HBM bytes of one gate/up grouped-GEMM launch.
 
     bytes = weights of the touched routed experts (2F x D each) + shared weights
             (1 byte per weight and a 4-byte scale per row with FP8 weights)
           + A rows read (k*T routed rows and T shared rows of width D)
           + h written ((k*T*F + T*Fs) elements).
+    shared=False: a launch over the routed experts only (the shared expert runs
+    in moe_shared_ffn).
     """
+    if not shared:
+        s = configs.variant(s, Fs=0)
     el = 2 if s.dtype == "bf16" else 4
     flops = 4.0 * s.S * s.D * s.F + 4.0 * s.T * s.D * s.Fs
     if fp8:
@@ -429,7 +433,7 @@ def main():
 
     counts = b.counts.cpu().numpy()
     n_touched = int(np.count_nonzero(counts))
-    flops, nbytes = gate_up_work(s, n_touched, args.fp8_weights)
+    flops, nbytes = gate_up_work(s, n_touched, args.fp8_weights, shared=not split)
     intensity = flops / nbytes
     peak_flops = PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_F32_TFLOPS
     ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -441,8 +445,9 @@ def main():
         achieved = flops / (gate_up_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_flops,
                 "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4)}
-    traffic = None if args.fp8_weights else measured_traffic(s.name)
+    traffic = None if (args.fp8_weights or split) else measured_traffic(s.name)
     kname = ("grouped_gemm_kernel<gate_up, FP8 weights> (moe_grouped_gate_up_fp8)" if args.fp8_weights
+             else "grouped_gemm_kernel<gate_up> (moe_grouped_gate_up, routed experts only)" if split
              else "grouped_gemm_kernel<gate_up> (moe_grouped_gate_up)")
     roof.update({"traffic": traffic, "kernel": kname,
                  "kernel_ms": round(gate_up_ms, 4), "algorithmic_bytes": nbytes,
