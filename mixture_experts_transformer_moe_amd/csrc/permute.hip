@@ -30,6 +30,23 @@ static_assert(kTB == kMaxE, "the scatter kernel keeps one thread per expert");
 
 __device__ __forceinline__ int clamp_e(int e, int E) { return e >= E ? E - 1 : e; }
 
+// Inclusive scan of one value per thread over a block of kTB threads: lane
+// shuffles within each wave, then the totals of the waves before (wtot: one
+// LDS word per wave).  Ends with every wave total read; the caller
+// synchronises before wtot is written again.
+__device__ __forceinline__ int block_inclusive_scan(int v, int32_t* wtot) {
+  const int ln = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int n = __shfl_up(v, d);
+    if (ln >= d) v += n;
+  }
+  if (ln == 63) wtot[w] = v;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) v += wtot[i];
+  return v;
+}
+
 __global__ __launch_bounds__(kTB) void perm_hist_kernel(const int32_t* __restrict__ idx, int T,
                                                         int E, int k, int32_t* __restrict__ blk) {
   __shared__ int32_t hist[kMaxE];
@@ -57,7 +74,7 @@ __global__ __launch_bounds__(kTB) void perm_scatter_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ slot_of) {
   __shared__ uint32_t chose[kMaxE][kTB / 32];   // bit (t mod 256) of row e: token chose e
   __shared__ int32_t base[kMaxE];
-  __shared__ int32_t scan[kMaxE];
+  __shared__ int32_t wtot[kTB / 64];
   const int e = threadIdx.x;                      // kTB == kMaxE: one thread per expert
   const int local = threadIdx.x;                  // and one per token of the block
   const int t = blockIdx.x * kTB + local;
@@ -87,21 +104,14 @@ __global__ __launch_bounds__(kTB) void perm_scatter_kernel(const int32_t* __rest
       before += b < static_cast<int>(blockIdx.x) ? c : 0;
     }
   }
-  scan[e] = total;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over the expert totals
-  for (int off = 1; off < kMaxE; off <<= 1) {
-    const int v = e >= off ? scan[e - off] : 0;
-    __syncthreads();
-    scan[e] += v;
-    __syncthreads();
-  }
-  const int excl = scan[e] - total;
+  // inclusive scan over the expert totals
+  const int incl = block_inclusive_scan(total, wtot);
+  const int excl = incl - total;
   base[e] = excl + before;
   if (blockIdx.x == 0 && e < E) {
     counts[e] = total;
     offsets[e] = excl;
-    if (e == E - 1) offsets[E] = scan[e];
+    if (e == E - 1) offsets[E] = incl;
   }
   __syncthreads();
   const int word = local >> 5;
@@ -140,6 +150,7 @@ __global__ __launch_bounds__(kTB) void perm_single_block_kernel(const int32_t* _
   __shared__ uint32_t chose[kMaxE][kTB / 32];   // bit t of row e: token t chose e
   __shared__ int32_t hist[kMaxE];
   __shared__ int32_t scan[kMaxE];
+  __shared__ int32_t wtot[kTB / 64];
   const int t = threadIdx.x;                      // token, and expert for the scan
   for (int i = t; i < kMaxE * (kTB / 32); i += kTB) (&chose[0][0])[i] = 0u;
   hist[t] = 0;
@@ -155,14 +166,8 @@ __global__ __launch_bounds__(kTB) void perm_single_block_kernel(const int32_t* _
     }
   __syncthreads();
   const int total = hist[t];
-  scan[t] = total;
+  scan[t] = block_inclusive_scan(total, wtot);
   __syncthreads();
-  for (int off = 1; off < kMaxE; off <<= 1) {
-    const int v = t >= off ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += v;
-    __syncthreads();
-  }
   if (t < E) {
     counts[t] = total;
     offsets[t] = scan[t] - total;
