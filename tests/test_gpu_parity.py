@@ -114,6 +114,11 @@ EDGE = {
     "rows150_T600_E32": dict(T=600, E=32, k=8),
     "rows256_T512_D512": dict(T=512, D=512, E=16, k=8),
     "rows350_T700_D512": dict(T=700, D=512, E=16, k=8, Fs=512),
+    # router block shapes at block counts that do not split evenly over the 8
+    # XCDs, with ragged token (and expert) tails: 64 x 64 blocks, 132 of them
+    "router64_T2050_E256": dict(T=2050, E=256, k=8),
+    # 32 x 32 blocks, 132 of them, 72 experts
+    "router32_T1400_E72": dict(T=1400, E=72, k=8),
 }
 
 
