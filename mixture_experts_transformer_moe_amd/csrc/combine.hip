@@ -12,15 +12,6 @@ namespace {
 
 constexpr int kMaxK = 16;
 
-__device__ __forceinline__ void load8(const bf16_t* p, float* v) {
-  const u32x4 q = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(q[i] << 16);
-    v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
-  }
-}
-
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const bf16_t* __restrict__ y_perm,
                                                            const bf16_t* __restrict__ y_shared,
                                                            const int32_t* __restrict__ slot_of,
@@ -49,21 +40,38 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const bf16_t* __restr
     kv_s = kv;
   }
   __syncthreads();
-  const int kv = kv_s;
+  const int kv = __builtin_amdgcn_readfirstlane(kv_s);
   for (int c = threadIdx.x * 8; c < D; c += blockDim.x * 8) {
+    // the shared row's chunk first: it needs no routing
+    u32x4 sh = {0u, 0u, 0u, 0u};
+    if (y_shared) sh = *reinterpret_cast<const u32x4*>(y_shared + static_cast<size_t>(t) * D + c);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < kv; ++j) {
-      float v[8];
-      load8(y_perm + static_cast<size_t>(slot_s[j]) * D + c, v);
-      const float cj = coef_s[j];
+    // the routed rows in batches of 8: a batch's loads all in flight together
+    // (a small batch of tokens has too few workgroups to hide one load's
+    // latency per slot), then the products in slot order
+    for (int j0 = 0; j0 < kv; j0 += 8) {
+      u32x4 q[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(cj, v[i], acc[i]);
+      for (int u = 0; u < 8; ++u)
+        q[u] = j0 + u < kv ? *reinterpret_cast<const u32x4*>(y_perm + static_cast<size_t>(slot_s[j0 + u]) * D + c)
+                           : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u >= kv) continue;
+        const float cj = coef_s[j0 + u];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(cj, __uint_as_float(q[u][i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(cj, __uint_as_float(q[u][i] & 0xffff0000u), acc[2 * i + 1]);
+        }
+      }
     }
     if (y_shared) {
-      float v[8];
-      load8(y_shared + static_cast<size_t>(t) * D + c, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = v[i] + acc[i];
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = __uint_as_float(sh[i] << 16) + acc[2 * i];
+        acc[2 * i + 1] = __uint_as_float(sh[i] & 0xffff0000u) + acc[2 * i + 1];
+      }
     }
     u32x4 o;
 #pragma unroll
