@@ -1,0 +1,56 @@
+"""bench.py's host-side parts: the one-GPU rule, the algorithmic work it prices
+the roofline with, and the source-keyed traffic records (no GPU needed)."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import pytest
+
+from mixture_experts_transformer_moe_amd import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def test_gate_up_work_counts_each_term_once(bench):
+    s = configs.XS2_T4096
+    flops, nbytes = bench.gate_up_work(s, n_touched=200)
+    # a matrix product of m x K by K x n is 2 m K n flops; gate and up are two of them
+    assert flops == 2 * (s.T * s.k) * s.D * (2 * s.F) + 2 * s.T * s.D * (2 * s.Fs)
+    weights = (200 * 2 * s.F * s.D + 2 * s.Fs * s.D) * 2
+    rows_in = (s.T * s.k + s.T) * s.D * 2
+    rows_out = (s.T * s.k * s.F + s.T * s.Fs) * 2
+    assert nbytes == weights + rows_in + rows_out
+    # routed experts only: every shared-expert term drops out
+    f2, b2 = bench.gate_up_work(s, n_touched=200, shared=False)
+    assert f2 == 2 * (s.T * s.k) * s.D * (2 * s.F)
+    assert b2 == 200 * 2 * s.F * s.D * 2 + s.T * s.k * s.D * 2 + s.T * s.k * s.F * 2
+    # FP8 weights: one byte per weight plus a 4-byte scale per weight row
+    f3, b3 = bench.gate_up_work(s, n_touched=200, fp8=True)
+    assert f3 == flops
+    assert b3 == (200 * 2 * s.F + 2 * s.Fs) * (s.D + 4) + rows_in + rows_out
+
+
+def test_traffic_records_hold_only_for_the_sources_they_were_taken_on(bench):
+    sha = bench.sources_sha256(bench.GEMM_SOURCES)
+    table = {"w": (100.0, 50.0, sha), "stale": (100.0, 50.0, "0" * 64)}
+    got = bench.measured_traffic("w", table, bench.GEMM_SOURCES)
+    assert got == pytest.approx(100.0 * 1024 * bench.FETCH_FACTOR + 50.0 * 1024 * bench.WRITE_FACTOR)
+    assert bench.measured_traffic("stale", table, bench.GEMM_SOURCES) is None
+    assert bench.measured_traffic("absent", table, bench.GEMM_SOURCES) is None
