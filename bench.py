@@ -107,9 +107,12 @@ def gate_up_work(s: configs.MoEShape, n_touched: int, fp8: bool = False, shared:
     return flops, float(w + a + h)
 
 
-def cpu_oracle_baseline(s, inp_host, target_s: float = 12.0, fp8: bool = False):
+def cpu_oracle_baseline(s, inp_host, target_s: float = 12.0, fp8: bool = False, gpu_topk=None):
     """Times the CPU oracle (self-contained fp64 forward) on host cores (with FP8
-    weights: the oracle's FP8 reading of every expert, quantised as it goes)."""
+    weights: the oracle's FP8 reading of every expert, quantised as it goes).
+    With gpu_topk ([T, k] expert ids from the GPU's fp32 logits) it also counts
+    the sampled tokens whose self-contained fp64 routing selects another set of
+    experts (near-ties between fp32 and fp64 logits; expected 0)."""
     from oracle import moe_oracle as O
     from oracle import fp8_oracle as F8
     wrap = F8.Fp8Weights if fp8 else (lambda inputs: inputs)
@@ -140,7 +143,7 @@ def cpu_oracle_baseline(s, inp_host, target_s: float = 12.0, fp8: bool = False):
     n = min(n, s.T)
     passes, tokens, t0 = 0, 0, time.perf_counter()
     while True:
-        O.forward(wrap(Sub(n)), s.alpha, s.k)
+        _, routing = O.forward(wrap(Sub(n)), s.alpha, s.k)
         passes += 1
         tokens += n
         el = time.perf_counter() - t0
@@ -148,8 +151,14 @@ def cpu_oracle_baseline(s, inp_host, target_s: float = 12.0, fp8: bool = False):
             break
     sample = (f"self-contained fp64 oracle forward{' with FP8 weights' if fp8 else ''} over the first {n} of {s.T} tokens "
               f"(all experts they select), {passes} pass(es), weights already in host memory")
-    return {"value": tokens / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample, "seconds": round(el, 3)}
+    res = {"value": tokens / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+           "sample": sample, "seconds": round(el, 3)}
+    if gpu_topk is not None:
+        cpu_sets = np.sort(np.asarray(routing.topk_idx)[:n], axis=1)
+        gpu_sets = np.sort(np.asarray(gpu_topk)[:n], axis=1)
+        res["routing_compared"] = int(n)
+        res["routing_differs"] = int(np.count_nonzero((cpu_sets != gpu_sets).any(axis=1)))
+    return res
 
 
 def wgrad_work(s: configs.MoEShape, routed_rows: int):
@@ -215,8 +224,14 @@ def cpu_train_baseline(s, inp_host, mask, dout, target_s: float = 12.0):
     sample = (f"fp64 training oracle (masked forward with its own routing, then the backward of every "
               f"expert touched, shared expert and router) over the first {n} of {s.T} tokens, "
               f"{passes} pass(es), weights already in host memory")
-    return {"value": tokens / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample, "seconds": round(el, 3)}
+    res = {"value": tokens / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+           "sample": sample, "seconds": round(el, 3)}
+    if gpu_topk is not None:
+        cpu_sets = np.sort(np.asarray(routing.topk_idx)[:n], axis=1)
+        gpu_sets = np.sort(np.asarray(gpu_topk)[:n], axis=1)
+        res["routing_compared"] = int(n)
+        res["routing_differs"] = int(np.count_nonzero((cpu_sets != gpu_sets).any(axis=1)))
+    return res
 
 
 def copy_calibration(mib: int, dev) -> None:
@@ -459,7 +474,7 @@ def main():
     layer_tflops = s.flops() / (ms * 1e-3) / 1e12
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_oracle_baseline(s, host, fp8=args.fp8_weights)
+        cpu = cpu_oracle_baseline(s, host, fp8=args.fp8_weights, gpu_topk=b.topk_idx.cpu().numpy())
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),

@@ -54,3 +54,23 @@ def test_traffic_records_hold_only_for_the_sources_they_were_taken_on(bench):
     assert got == pytest.approx(100.0 * 1024 * bench.FETCH_FACTOR + 50.0 * 1024 * bench.WRITE_FACTOR)
     assert bench.measured_traffic("stale", table, bench.GEMM_SOURCES) is None
     assert bench.measured_traffic("absent", table, bench.GEMM_SOURCES) is None
+
+
+def test_cpu_baseline_counts_tokens_routed_to_another_expert_set(bench):
+    import numpy as np
+    from mixture_experts_transformer_moe_amd import inputs as I
+    from oracle import moe_oracle as O
+    s = configs.TINY_F32
+    li = I.make_inputs(s)
+    wgu, wd = li.all_experts()
+    host = {"x": li.x, "w_router": li.w_router, "bias": li.bias, "wgu": wgu, "wd": wd,
+            "shared": li.shared()}
+    _, r = O.forward(li, s.alpha, s.k)
+    idx = np.asarray(r.topk_idx).copy()
+    res = bench.cpu_oracle_baseline(s, host, target_s=0.2, gpu_topk=idx[:, ::-1])
+    assert res["kind"] == "oracle" and res["value"] > 0 and res["cores"] >= 1
+    assert res["routing_compared"] == s.T and res["routing_differs"] == 0   # same sets, any order
+    other = next(e for e in range(s.E) if e not in idx[5])
+    idx[5, 1] = other
+    res = bench.cpu_oracle_baseline(s, host, target_s=0.2, gpu_topk=idx)
+    assert res["routing_differs"] == 1
