@@ -393,16 +393,22 @@ def main():
         ev_done.record(stream)
         h_shared = b.h[s.T * s.k * s.F:]
 
-    def step(ev=None):
+    def step(ev=None, marks=None):
+        def mark(i):
+            if marks is not None:
+                marks[i].record(stream)
         if split:
             # the shared expert on a second stream, beside the router and the
             # permutation; it rewrites y_shared once the previous combine is done
             side.wait_event(ev_done)
             binding.moe_shared_ffn(c, x, w.ws_gate_up, w.ws_down, h_shared, b.y_shared, side)
             ev_shared.record(side)
+        mark(0)
         binding.moe_route(c, x, w.w_router, w.bias, b.logits, b.topk_idx, b.topk_w, stream)
+        mark(1)
         binding.moe_permute(c, b.topk_idx, x, b.counts, b.offsets, b.sorted_token, b.slot_of,
                             b.x_perm, b.workspace, stream)
+        mark(2)
         if ev is not None:
             ev[0].record(stream)
         if w.fp8:
@@ -414,15 +420,18 @@ def main():
                                         None if split else w.ws_gate_up, b.h, stream)
         if ev is not None:
             ev[1].record(stream)
+        mark(3)
         if w.fp8:
             binding.moe_grouped_down_fp8(c, b.h, b.offsets, w.w_down, w.w_down_scale, w.ws_down,
                                          w.ws_down_scale, b.y_perm, b.y_shared, stream)
         else:
             binding.moe_grouped_down(c, b.h, b.offsets, w.w_down, None if split else w.ws_down,
                                      b.y_perm, b.y_shared, stream)
+        mark(4)
         if split:
             stream.wait_event(ev_shared)
         binding.moe_combine(c, b.y_perm, b.y_shared, b.slot_of, b.topk_w, b.out, stream)
+        mark(5)
         if split:
             ev_done.record(stream)
 
@@ -442,6 +451,19 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gate_up_ms = float(np.mean([a.elapsed_time(z) for a, z in evs.values()]))
+
+    # per-call medians (untimed pass after the timed steps: events between the
+    # calls on the layer's stream, 20 steps after 5 warmup ones)
+    calls = ("route", "permute", "gate_up", "down", "combine")
+    per_call = {n: [] for n in calls}
+    for i in range(25):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        step(marks=marks)
+        torch.cuda.synchronize()
+        if i >= 5:
+            for j, n in enumerate(calls):
+                per_call[n].append(marks[j].elapsed_time(marks[j + 1]))
+    calls_ms = {n: round(float(np.median(v)), 4) for n, v in per_call.items()}
 
     if args.copy_mib > 0:
         copy_calibration(args.copy_mib, dev)
@@ -487,6 +509,8 @@ def main():
                    "parallelism": "single-gpu"},
         "layer_tflops": round(layer_tflops, 1),
         "experts_touched": n_touched, "rows_per_expert_max": int(counts.max()),
+        "calls_median_ms": calls_ms,
+        "tokens_per_s_from_call_medians": round(s.T / (sum(calls_ms.values()) * 1e-3), 1),
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
