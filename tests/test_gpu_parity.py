@@ -73,6 +73,12 @@ def test_small_bf16_full_parity_ragged():
     full_parity(SMALL_BF16)
 
 
+@pytest.mark.parametrize("seed", [21, 22, 23])
+def test_small_bf16_full_parity_other_seeds(seed):
+    # other inputs and weights of the same ragged shape
+    full_parity(configs.variant(SMALL_BF16, name=f"small_bf16_seed{seed}", seed=seed))
+
+
 def test_small_bf16_gather_mode_matches_x_perm_mode():
     s = SMALL_BF16
     inp = StackedInputs(LayerInputs(s))

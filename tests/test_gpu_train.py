@@ -117,6 +117,12 @@ def test_small_with_padding_and_aux_loss():
     full_parity(SMALL)
 
 
+@pytest.mark.parametrize("seed", [21, 22, 23])
+def test_small_other_seeds(seed):
+    # other inputs, weights and padding patterns of the same shape
+    full_parity(configs.variant(SMALL, name=f"train_small_seed{seed}", seed=seed))
+
+
 def test_small_x_perm_mode():
     full_parity(SMALL, gather=False)
 
