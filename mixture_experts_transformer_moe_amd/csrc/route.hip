@@ -132,8 +132,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 // smallest batches: 4 times the workgroups, each reading half the rows;
 // v_mfma_f32_16x16x32_bf16): lane l holds token (l mod 16) and experts
 // 4 (l / 16) + 0..3.
-template <int TM, int TN, int KS, int NS>
-__global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __restrict__ x,
+template <int TM, int TN, int KS, int NS, int NW = 4>
+__global__ __launch_bounds__(64 * NW, 1) void route_bf16_kernel(const bf16_t* __restrict__ x,
                                                             const bf16_t* __restrict__ wr,
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ logits, int T, int D,
@@ -143,8 +143,8 @@ __global__ __launch_bounds__(256, 1) void route_bf16_kernel(const bf16_t* __rest
   constexpr int kBlockElems = kRows * kPipeBK;
   constexpr int kStageElems = KS * kBlockElems;
   constexpr int kLoads = KS * kRows / 8;               // 1 KB loads per stage
-  constexpr int LPW = kLoads / 4;                      // per wave
-  static_assert((TM / MF) * (TN / MF) * KS == 4 && kLoads % 4 == 0, "4 waves, equal loads per stage");
+  constexpr int LPW = kLoads / NW;                     // per wave
+  static_assert((TM / MF) * (TN / MF) * KS == NW && kLoads % NW == 0, "NW waves, equal loads per stage");
   static_assert(MF == 32 || (TM == 16 && TN == 16), "16 x 16 blocks: one per wave");
   static_assert(NS * kStageElems * 2 <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) bf16_t lds[NS * kStageElems];
@@ -302,9 +302,13 @@ hipError_t launch_route_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* 
   // loads in flight per CU do not grow past a few stages' worth, and every
   // stage beyond that adds clamped repeat loads at the end of the K loop
   // (measured: 4 stages 11 to 16% faster than 8 on 8192 and 32768 tokens)
+  const int huge = ((s.T + 127) / 128) * ((s.E + 63) / 64);
   const int big = ((s.T + 63) / 64) * ((s.E + 63) / 64);
   const int mid = ((s.T + 31) / 32) * ((s.E + 31) / 32);
-  if (big >= 128) {
+  if (huge >= 256) {
+    // 128 x 64 blocks, 8 waves: a quarter fewer bytes into LDS per logit
+    route_bf16_kernel<128, 64, 1, 4, 8><<<huge, 512, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
+  } else if (big >= 128) {
     route_bf16_kernel<64, 64, 1, 4><<<big, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
   } else if (mid >= 128) {
     route_bf16_kernel<32, 32, 4, 4><<<mid, 256, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);

@@ -125,6 +125,8 @@ EDGE = {
     "router64_T2050_E256": dict(T=2050, E=256, k=8),
     # 32 x 32 blocks, 132 of them, 72 experts
     "router32_T1400_E72": dict(T=1400, E=72, k=8),
+    # 128 x 64 blocks (8 waves), 260 of them, a ragged token tail
+    "router128_T8200_E256": dict(T=8200, E=256, k=2),
 }
 
 
