@@ -224,14 +224,8 @@ def cpu_train_baseline(s, inp_host, mask, dout, target_s: float = 12.0):
     sample = (f"fp64 training oracle (masked forward with its own routing, then the backward of every "
               f"expert touched, shared expert and router) over the first {n} of {s.T} tokens, "
               f"{passes} pass(es), weights already in host memory")
-    res = {"value": tokens / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-           "sample": sample, "seconds": round(el, 3)}
-    if gpu_topk is not None:
-        cpu_sets = np.sort(np.asarray(routing.topk_idx)[:n], axis=1)
-        gpu_sets = np.sort(np.asarray(gpu_topk)[:n], axis=1)
-        res["routing_compared"] = int(n)
-        res["routing_differs"] = int(np.count_nonzero((cpu_sets != gpu_sets).any(axis=1)))
-    return res
+    return {"value": tokens / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample, "seconds": round(el, 3)}
 
 
 def copy_calibration(mib: int, dev) -> None:

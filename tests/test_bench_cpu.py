@@ -74,3 +74,16 @@ def test_cpu_baseline_counts_tokens_routed_to_another_expert_set(bench):
     idx[5, 1] = other
     res = bench.cpu_oracle_baseline(s, host, target_s=0.2, gpu_topk=idx)
     assert res["routing_differs"] == 1
+
+
+def test_cpu_training_baseline_runs_on_a_small_padded_batch(bench):
+    from mixture_experts_transformer_moe_amd import inputs as I
+    s = configs.variant(configs.XS2_TRAIN_T4096, name="bench_train_tiny", T=96, D=256, E=16, k=4,
+                        F=256, Fs=256, seq_len=32)
+    li = I.make_inputs(s)
+    wgu, wd = li.all_experts()
+    host = {"x": li.x, "w_router": li.w_router, "bias": li.bias, "wgu": wgu, "wd": wd,
+            "shared": li.shared()}
+    res = bench.cpu_train_baseline(s, host, I.token_mask(s), I.dout_encoded(s), target_s=0.2)
+    assert res["kind"] == "oracle" and res["unit"] == "tokens/s" and res["value"] > 0
+    assert res["cores"] >= 1 and "training oracle" in res["sample"]
