@@ -118,8 +118,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
 }
 
-// Router logits, bf16: a workgroup of 4 waves computes a TM x TN block of
-// logits (tokens x experts) over the whole of D.  Wave w sits at (tm, tn, ks):
+// Router logits, bf16: a workgroup of NW waves (4, or 8 for 128 x 64 blocks)
+// computes a TM x TN block of logits (tokens x experts) over the whole of D.
+// Wave w sits at (tm, tn, ks):
 // it owns the MF x MF block (tm, tn) and, when the four waves split K (KS = 4
 // for small batches, so that few tokens still keep 4 load streams per CU),
 // the K blocks ks, ks + KS, ...; the partial blocks are summed in LDS in ks
@@ -296,6 +297,7 @@ hipError_t launch_topk(const moe_shape& s, const float* logits, const uint8_t* m
 hipError_t launch_route_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* wr,
                              const float* bias, const uint8_t* mask, float* logits, int32_t* idx,
                              float* w, hipStream_t st) {
+  // 128 x 64 blocks of 8 waves when there are at least as many as CUs, else
   // 64 x 64 blocks when they are enough to fill the chip, else 32 x 32 blocks
   // with the K split over the workgroup's waves, else (fewer than half as many
   // as there are CUs) 16 x 16 blocks.  The stages are few: the
