@@ -27,6 +27,7 @@ namespace {
 constexpr int kMaxK = 16;
 constexpr int kDzLd = 256;        // row stride of the bf16 logit gradient (E padded to 256)
 constexpr int kStatRows = 16;     // token rows per block of the column sums
+constexpr int kMaxE = 256;        // the experts a router row holds at most
 
 __device__ __forceinline__ void load8(const bf16_t* p, float* v) {
   const u32x4 q = *reinterpret_cast<const u32x4*>(p);
@@ -305,28 +306,52 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const float* __rest
   const int t0 = blockIdx.x * kStatRows;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (kStats) {
-    // Q_t = sum_e sigma(z_te); 0 marks a padding token (or a row past T)
-    for (int r = wave; r < kStatRows; r += 4) {
-      const int t = t0 + r;
+    // Q_t = sum_e sigma(z_te); 0 marks a padding token (or a row past T).
+    // The wave's rows r = wave + 4 i, lane's experts e = lane + 64 j: every
+    // load first (all in flight), then the sums in the same order as a plain
+    // loop would take them.
+    constexpr int kRowsPerWave = kStatRows / 4;
+    float z[kRowsPerWave][kMaxE / 64];
+    int first[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int t = t0 + wave + 4 * i;
+      first[i] = t < T ? topk_idx[static_cast<size_t>(t) * k] : -1;
+#pragma unroll
+      for (int j = 0; j < kMaxE / 64; ++j) {
+        const int e = lane + 64 * j;
+        z[i][j] = (t < T && e < E) ? m[static_cast<size_t>(t) * E + e] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int r = wave + 4 * i, t = t0 + r;
       float s = 0.f;
-      if (t < T)
-        for (int e = lane; e < E; e += 64) s += sigmoidf(m[static_cast<size_t>(t) * E + e]);
+#pragma unroll
+      for (int j = 0; j < kMaxE / 64; ++j)
+        if (t < T && lane + 64 * j < E) s += sigmoidf(z[i][j]);
       s = wave_sum(s);
-      if (lane == 0) q_s[r] = (t < T && topk_idx[static_cast<size_t>(t) * k] >= 0) ? s : 0.f;
+      if (lane == 0) q_s[r] = (t < T && first[i] >= 0) ? s : 0.f;
     }
     __syncthreads();
   }
   const int e = tid;
   if (e >= E) return;
-  float acc = 0.f;
+  // the column's rows, all loads in flight, then added in row order
+  float v[kStatRows];
+#pragma unroll
   for (int r = 0; r < kStatRows; ++r) {
     const int t = t0 + r;
-    if (t >= T) break;
-    const float v = m[static_cast<size_t>(t) * E + e];
+    v[r] = t < T ? m[static_cast<size_t>(t) * E + e] : 0.f;
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int r = 0; r < kStatRows; ++r) {
+    if (t0 + r >= T) continue;
     if (kStats) {
-      if (q_s[r] > 0.f) acc += sigmoidf(v) / q_s[r];
+      if (q_s[r] > 0.f) acc += sigmoidf(v[r]) / q_s[r];
     } else {
-      acc += v;
+      acc += v[r];
     }
   }
   part[static_cast<size_t>(blockIdx.x) * E + e] = acc;
