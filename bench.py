@@ -55,7 +55,7 @@ WRITE_FACTOR = 1.0
 GEMM_SOURCES = ("grouped_gemm.hip", "mma_stream.h", "lds_dma.h", "moe_internal.h")
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
-    "xs2_bf16_t4096_d2048": (663903.6, 37045.7,
+    "xs2_bf16_t4096_d2048": (662779.1, 37054.2,
                              "45cf557f44914b82175ec326ecca5e4ebdc36c2c4b79d39d8b25e2746143d312"),
 }
 
@@ -63,7 +63,7 @@ TRAFFIC = {
 # The same for one launch of the weight-gradient kernel in the training pass.
 WGRAD_SOURCES = ("wgrad.hip", "lds_dma.h", "moe_internal.h")
 WGRAD_TRAFFIC = {
-    "xs2_train_bf16_t4096_d2048": (250784.4, 1581070.6,
+    "xs2_train_bf16_t4096_d2048": (250806.5, 1581073.2,
                                    "ec40073f6eb5ff1c325864b70a7ecb9ecbf6943d6d6224261cb66c932b35412f"),
 }
 
