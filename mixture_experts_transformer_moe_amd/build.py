@@ -20,7 +20,7 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_gemm.hip", "ffn_f32.hip", "combine.hip",
+SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_gemm.hip", "grouped_gemm_lds.hip", "ffn_f32.hip", "combine.hip",
            "pack.hip", "train.hip", "wgrad.hip"]
 
 CFLAGS = [

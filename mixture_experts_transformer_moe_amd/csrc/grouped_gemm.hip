@@ -29,34 +29,15 @@
 //     registers before one rounding to bf16;
 //   * a tile's outputs are stored while the next tile's loads stream (see the
 //     epilogue), 16 bytes per lane after a lane-pair swap.
+#include "grouped_gemm.h"
 #include "mma_stream.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = kPipeThreads;
-constexpr int kMaxE = 256;
-constexpr int kXcds = 8;
-
-enum Mode { kGateUp = 0, kDown = 1 };
-
-struct GemmArgs {
-  const bf16_t* a_routed;   // [S, K] rows in expert order (x_perm or h), or x when gather != null
-  const int32_t* gather;    // sorted_token (A row p = x[gather[p]]) or null
-  const bf16_t* a_shared;   // [T, Ks]
-  const unsigned char* w_routed;   // E packed [Nw, K] matrices (bf16, or FP8 codes)
-  const unsigned char* w_shared;   // packed [Nws, Ks]
-  const float* s_routed;    // FP8 weights: per-row scales [E, Nw] (else unused)
-  const float* s_shared;    //   [Nws]
-  bf16_t* out_routed;       // [S, N]
-  bf16_t* out_shared;       // [T, Ns]
-  const int32_t* offsets;   // [E + 1]
-  int T, E, S;
-  int K, Ks;                // reduction length (routed / shared)
-  int N, Ns;                // output columns (routed / shared)
-  int has_shared;
-  int spread_shared;        // shared-expert tiles spread through the schedule (else last)
-};
+constexpr int kMaxE = kGemmMaxE;
+constexpr int kXcds = kGemmXcds;
 
 // Output side of one tile.
 template <int NB>
@@ -406,19 +387,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   stream_finish();
 }
 
-int persistent_grid() {
-  static int grid = 0;
-  if (grid == 0) {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-      hipDeviceProp_t p;
-      if (hipGetDeviceProperties(&p, dev) == hipSuccess && p.multiProcessorCount > 0)
-        cus = p.multiProcessorCount;
-    }
-    grid = ((cus + kXcds - 1) / kXcds) * kXcds;   // one workgroup per CU
-  }
-  return grid;
-}
 
 // Tile shape by the mean rows per expert (k*T/E).  Up to ~200 rows the weight
 // stream from HBM is the limit: tall row blocks (an expert's rows mostly fit
@@ -434,6 +402,11 @@ hipError_t launch_tiles(const GemmArgs& a, int mean_rows, hipStream_t st) {
   // steps) of FP8 ones
   constexpr int P = W8 ? 8 : 16;
   const int wide = MODE == kGateUp ? 256 : 512;            // output columns of an NB = 4 tile
+  // From ~768 rows per expert the LDS-tiled kernel's 256-row tiles hold most
+  // of an expert's rows in full tiles (measured faster at 1024 rows per expert,
+  // slower at 256 and 512, where the short last row tile of each expert
+  // streams its weights for few rows)
+  if (!W8 && mean_rows >= 768 && lds_gemm_fits(MODE, a)) return launch_lds_gemm(MODE, a, st);
   if (mean_rows >= 192 && a.N % wide == 0 && (!a.has_shared || a.Ns % wide == 0))
     grouped_gemm_kernel<MODE, 96, 4, 8, W8><<<persistent_grid(), kThreads, 0, st>>>(a);
   else if (mean_rows >= 96)
@@ -491,6 +464,20 @@ GemmArgs down_args(const moe_shape& s, const bf16_t* h, const int32_t* offsets, 
 }
 
 }  // namespace
+
+int persistent_grid() {
+  static int grid = 0;
+  if (grid == 0) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      hipDeviceProp_t p;
+      if (hipGetDeviceProperties(&p, dev) == hipSuccess && p.multiProcessorCount > 0)
+        cus = p.multiProcessorCount;
+    }
+    grid = ((cus + kXcds - 1) / kXcds) * kXcds;   // one workgroup per CU
+  }
+  return grid;
+}
 
 // ---- training pass: the same kernel in its plain mode (no SwiGLU) on other
 // operands.  Packed transposed weights (moe_pack_weights_transposed) turn the

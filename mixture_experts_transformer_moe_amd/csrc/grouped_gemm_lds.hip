@@ -1,0 +1,563 @@
+// Grouped GEMMs for batches with many rows per expert: 256 x 256 tiles with
+// both operands staged in LDS, bf16 MFMA with fp32 accumulation.
+//
+// What they compute is what grouped_gemm.hip computes ("Laguna-M.1-base",
+// Feed-forward: SwiGLU without biases; the grouped GEMM over expert-ordered
+// tokens of "Laguna M.1/XS.2 Technical Report", Key claims, report section
+// 3.1.2):  gate_up  h[p] = silu(Wg_e a_p) * (Wu_e a_p),  down  y[p] = Wd_e h[p],
+// the shared expert as one more group over all T rows; the plain mode (down)
+// also serves the training pass's products.
+//
+// Why a second kernel: once an expert has a few hundred rows the MFMA pipes,
+// not the HBM weight stream, set the pace, and the limit becomes the bytes a
+// CU pulls through its load path per MFMA.  A tile of 256 token rows x 256
+// weight rows with both operands in LDS pulls 0.25 KB per 32x32x16 MFMA (32
+// bytes per clock per CU at the full MFMA rate), which the load path sustains
+// from L2 (about 45-50 bytes per clock per CU measured on this part), provided
+// that the tiles sharing operands run together behind one L2.
+//
+// Design:
+//   * persistent grid, one workgroup of 4 waves per CU; the tile table is built
+//     on the device from `offsets` (no host synchronisation); the shared group's
+//     tiles come first, then the routed experts'; inside a group the output
+//     column blocks of one row block are adjacent, and tiles go out in rounds of
+//     one per workgroup, each round cut into 8 runs of consecutive tiles, one
+//     run per XCD, so the tiles of one expert run at the same time behind one
+//     L2 and walk K in step;
+//   * waves in a 2 x 2 grid: wave (r, c) owns 4 token blocks x 4 weight blocks
+//     of 32 (256 fp32 accumulators per lane); token block b of the tile goes to
+//     wave row b mod 2, so a ragged last row block of an expert splits its
+//     blocks evenly over both wave rows, and a wave skips the MFMAs of blocks
+//     that hold no row;
+//   * K advances in stages of 32 through a ring of 4 LDS stages of 32 KB (token
+//     rows, then weight blocks), filled by direct global->LDS loads
+//     (global_load_lds_dwordx4): token rows gathered through `sorted_token`
+//     land as 16 rows x 64 bytes per wave load, XOR-swizzled for conflict-free
+//     ds_read_b128; packed weights land as 1 KB MFMA operand blocks;
+//   * one barrier per stage, between its two MFMA steps: by then every wave has
+//     read the stage before it (whose buffer then takes the stage three ahead)
+//     and each wave has waited for its own loads of the next stage; MFMA
+//     operands are read from LDS one step ahead into a second register set;
+//   * the ring does not drain between tiles: the last stages of a tile load the
+//     next tile's first three stages, and the tile's outputs are stored after
+//     them (a constant number of 16-byte stores per wave: rows past a tile's
+//     last rewrite its last row, skipped blocks rewrite the wave's first block,
+//     with the same bits), so the next tile's first waits can count them;
+//   * gate_up pairs each wave's two gate blocks with the up blocks of the same
+//     columns, so SwiGLU is applied in registers before one rounding to bf16.
+#include "grouped_gemm.h"
+#include <utility>
+
+#include "mma_stream.h"
+
+namespace moe {
+namespace {
+
+constexpr int kLThreads = 256;
+constexpr int kLBM = 256;                 // token rows per tile
+constexpr int kLBN = 256;                 // weight rows per tile
+constexpr int kLBK = 32;                  // K per LDS stage (two 16-wide MFMA steps)
+constexpr int kLNS = 4;                   // LDS stages
+constexpr int kLStageA = kLBM * kLBK * 2; // 16 KB of token rows
+constexpr int kLStage = kLStageA + kLBN * kLBK * 2;   // + 16 KB of weight blocks
+constexpr int kLLoads = 8;                // direct loads per wave and stage
+
+// Chunk swizzle of a 64-byte token row in LDS: 16-byte chunk c of tile row r
+// sits at slot c ^ lswz(r).  A ds_read_b128 of 32 rows, one chunk each, then
+// hits distinct slots in every group of 16 consecutive rows (4 rows of a
+// 256-byte bank window) and of 8 consecutive rows (2 rows of 128 bytes).
+__device__ __forceinline__ int lswz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// s_waitcnt vmcnt(kLLoads * later + (stores ? ST : 0)), later in {0, 1, 2}:
+// the waits below are compile-time constants chosen at run time.
+template <int ST>
+__device__ __forceinline__ void wait_vm(int later, bool stores) {
+  if (stores) {
+    if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLLoads + ST));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(kLLoads + ST));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_only(ST));
+  } else {
+    if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLLoads));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(kLLoads));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  }
+}
+
+// s_waitcnt immediate that waits for lgkmcnt <= n only (gfx9 encoding).
+constexpr int lgkmcnt_only(int n) { return 15 | (7 << 4) | ((n & 15) << 8) | (3 << 14); }
+
+// The order in which a step's MFMAs first use its operands (token block 0,
+// weight blocks 0-3, token blocks 1-3): read r of a step fetches operand
+// op_order(r).
+constexpr int op_order(int r) { return r == 0 ? 0 : (r <= 4 ? 3 + r : r - 4); }
+template <int R>
+using OpAt = std::integral_constant<int, op_order(R)>;
+
+// f(integral_constant<int, I>) for I = 0 .. N - 1, unrolled at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Sources of one tile (everything uniform except a_off).
+struct LTile {
+  const unsigned char* a;      // token rows: the chunk of load i of K stage kb is at a + 64 kb + a_off[i]
+  uint32_t a_off[4];
+  const unsigned char* w[2];   // the wave's two weight blocks: K stage kb, step s at w[j] + 2048 kb + 1024 s
+  int nkb;                     // K / 32
+  int nv;                      // token blocks of this wave that hold rows (1..4)
+  int tb0;                     // tile block of the wave's first block (the wave row, or 0)
+  bf16_t* out;                 // output element (tile row r, column c of the wave) at out + r * ld + c
+  int ld;
+  int valid;                   // rows of the tile
+};
+
+// A pointer that is the same in every lane, made visibly so (SGPRs).
+template <typename T>
+__device__ __forceinline__ const T* uni(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+  return reinterpret_cast<const T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// One direct global->LDS load: 16 bytes per lane from base + voff (lane l's
+// bytes land at LDS byte lds + off + 16 l).  base and lds are uniform (SGPRs),
+// off a constant.  The scalar add that forms m0 writes SCC, so SCC is listed
+// as clobbered (a carry the compiler keeps live across the block, between the
+// halves of a 64-bit address add, would otherwise be overwritten).
+template <int OFF>
+__device__ __forceinline__ void dma_lds(const unsigned char* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds), "i"(OFF)
+               : "memory", "m0", "scc");
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kLNS * kLStage];
+  __shared__ int tile_end[kGemmMaxE + 1];
+  __shared__ int row_base[kGemmMaxE + 1];
+  static_assert(kLNS * kLStage + 2 * (kGemmMaxE + 1) * 4 <= 160 * 1024, "LDS");
+  constexpr int kOutCols = MODE == kGateUp ? kLBN / 2 : kLBN;    // output columns per tile
+  constexpr int kJ = MODE == kGateUp ? 2 : 4;                    // output blocks of 32 per wave
+  constexpr int kStores = 4 * kJ * 2;                            // 16-byte stores per wave and tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int E = g.E;
+  const int nt_r = g.N / kOutCols;
+  const int nt_s = g.has_shared ? g.Ns / kOutCols : 0;
+  const int n_sh = g.has_shared ? (g.T + kLBM - 1) / kLBM * nt_s : 0;
+  const int G = gridDim.x;
+
+  // ---- tile table of the routed groups: tiles per expert, inclusive scan
+  {
+    int cnt = 0;
+    if (tid < E) {
+      // clamped so that no offsets table can move a tile outside [0, S)
+      const int lo = min(max(g.offsets[tid], 0), g.S);
+      const int hi = min(max(g.offsets[tid + 1], lo), g.S);
+      row_base[tid] = lo;
+      cnt = (hi - lo + kLBM - 1) / kLBM * nt_r;
+    }
+    const int ln = tid & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(cnt, d);
+      if (ln >= d) cnt += v;
+    }
+    if (ln == 63) tile_end[tid] = cnt;
+    __syncthreads();
+    for (int w = 0; w < (tid >> 6); ++w) cnt += tile_end[64 * w + 63];
+    __syncthreads();
+    tile_end[tid] = cnt;
+    if (tid == 0) row_base[E] = E > 0 ? min(max(g.offsets[E], row_base[E - 1]), g.S) : 0;
+    __syncthreads();
+  }
+  const int total = n_sh + (E > 0 ? __builtin_amdgcn_readfirstlane(tile_end[E - 1]) : 0);
+
+  // ---- rounds of G tiles, each cut into 8 runs of consecutive tiles, one per
+  // XCD (workgroup b runs on XCD b mod 8); a short last round is split evenly
+  // over the XCDs
+  const int xcd = blockIdx.x % kGemmXcds, in_xcd = blockIdx.x / kGemmXcds;
+  auto tile_at = [&](int r) -> int {
+    const int base = r * G;
+    if (base >= total) return -1;
+    const int n = min(G, total - base);
+    if (n == G) return base + xcd * (G / kGemmXcds) + in_xcd;
+    const int q = n / kGemmXcds, rem = n % kGemmXcds;
+    if (in_xcd >= q + (xcd < rem ? 1 : 0)) return -1;
+    return base + xcd * q + min(xcd, rem) + in_xcd;
+  };
+
+  // ---- sources and output of schedule slot ti
+  auto decode = [&](int ti, LTile& t) __attribute__((always_inline)) {
+    int ln = tid & 63;
+    asm volatile("" : "+v"(ln));      // per-lane arithmetic stays inside decode
+    const bool shared = ti < n_sh;
+    int grp = E, local = ti, first = 0;
+    if (!shared) {
+      const int r = ti - n_sh;
+      int lo = 0, hi = E - 1;         // first group with tile_end > r
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (tile_end[mid] > r) hi = mid; else lo = mid + 1;
+      }
+      grp = __builtin_amdgcn_readfirstlane(lo);
+      first = grp == 0 ? 0 : __builtin_amdgcn_readfirstlane(tile_end[grp - 1]);
+      local = r - first;
+    }
+    const int rb = shared ? 0 : __builtin_amdgcn_readfirstlane(row_base[grp]);
+    const int M = shared ? g.T : __builtin_amdgcn_readfirstlane(row_base[grp + 1]) - rb;
+    const int nt = shared ? nt_s : nt_r;
+    const int m0 = (local / nt) * kLBM;
+    const int n0 = (local % nt) * kOutCols;
+    const int K = shared ? g.Ks : g.K;
+    const int Nout = shared ? g.Ns : g.N;
+    const int valid = min(kLBM, M - m0);
+    const int mb = (valid + 31) >> 5;                    // token blocks that hold rows
+    const int nv_raw = wr == 0 ? (mb + 1) >> 1 : mb >> 1;
+    t.nv = nv_raw > 0 ? nv_raw : 1;
+    t.tb0 = nv_raw > 0 ? wr : 0;
+    t.nkb = K / kLBK;
+    t.valid = valid;
+
+    // token rows: load i of this wave fills tile rows 64 wave + 16 i + 0..15,
+    // lane l row 64 wave + 16 i + l / 4, LDS slot l % 4 = logical chunk
+    // (l % 4) ^ lswz(row); rows past the tile's last repeat it
+    const bool gathered = !shared && g.gather != nullptr;
+    if (gathered) {
+      // token ids by vector loads (one per lane and load): the compiler waits
+      // for them with everything in flight, once per tile
+      const int32_t* gt = g.gather + rb + m0;
+      t.a = uni(reinterpret_cast<const unsigned char*>(g.a_routed));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 64 * wave + 16 * i + (ln >> 2);
+        const int tok = min(max(gt[min(row, valid - 1)], 0), g.T - 1);
+        const int c = (ln & 3) ^ lswz(row);
+        t.a_off[i] = (static_cast<uint32_t>(tok) * static_cast<uint32_t>(K) + 8u * c) * 2u;
+      }
+    } else {
+      t.a = uni(reinterpret_cast<const unsigned char*>(shared ? g.a_shared + static_cast<size_t>(m0) * K
+                                                              : g.a_routed + static_cast<size_t>(rb + m0) * K));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 64 * wave + 16 * i + (ln >> 2);
+        const int c = (ln & 3) ^ lswz(row);
+        const int r = min(row, valid - 1);
+        t.a_off[i] = (static_cast<uint32_t>(r) * static_cast<uint32_t>(K) + 8u * c) * 2u;
+      }
+    }
+    // weight blocks this wave loads: tile weight blocks 2 wave and 2 wave + 1
+    // (gate_up: blocks 0-3 are gate rows n0.., blocks 4-7 the up rows of the
+    // same columns)
+    const int Nw = MODE == kGateUp ? 2 * Nout : Nout;
+    const unsigned char* wmat = shared ? g.w_shared : g.w_routed + static_cast<size_t>(grp) * Nw * K * 2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int blk = 2 * wave + j;
+      const int wrow = MODE == kGateUp ? (blk < 4 ? n0 + 32 * blk : Nout + n0 + 32 * (blk - 4)) : n0 + 32 * blk;
+      t.w[j] = uni(wmat + static_cast<size_t>(wrow >> 5) * K * 64);
+    }
+    // output: the wave's columns
+    const int col0 = n0 + (MODE == kGateUp ? 64 : 128) * wc;
+    t.out = (shared ? g.out_shared + static_cast<size_t>(m0) * Nout
+                    : g.out_routed + static_cast<size_t>(rb + m0) * Nout) + col0;
+    t.ld = Nout;
+  };
+
+  // direct loads of one K stage into a ring buffer, in two halves issued at
+  // different points: the token-row half (load i of 4, rows 64 wave + 16 i +
+  // lane / 4) and the weight half (load i of 4: block i / 2, step i % 2).
+  // lbw(buf): the LDS byte address of this wave's first 1 KB slot in buffer buf
+  const uint32_t lds0 = lds_addr(smem) + 4 * 1024 * wave;
+  auto lbw = [&](int buf) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds0 + static_cast<uint32_t>(buf) * kLStage));
+  };
+  const uint32_t vb[2] = {static_cast<uint32_t>(lane) * 16u, static_cast<uint32_t>(lane) * 16u + 1024u};
+  auto issue_a = [&](const unsigned char* src, const uint32_t (&aoff)[4], uint32_t lb, int i) __attribute__((always_inline)) {
+    switch (i) {
+      case 0: dma_lds<0>(src, aoff[0], lb); break;
+      case 1: dma_lds<1024>(src, aoff[1], lb); break;
+      case 2: dma_lds<2048>(src, aoff[2], lb); break;
+      default: dma_lds<3072>(src, aoff[3], lb); break;
+    }
+  };
+  auto issue_b = [&](const unsigned char* w0, const unsigned char* w1, uint32_t lb, int i) __attribute__((always_inline)) {
+    switch (i) {
+      case 0: dma_lds<kLStageA>(w0, vb[0], lb); break;
+      case 1: dma_lds<kLStageA + 1024>(w0, vb[1], lb); break;
+      case 2: dma_lds<kLStageA + 2048>(w1, vb[0], lb); break;
+      default: dma_lds<kLStageA + 3072>(w1, vb[1], lb); break;
+    }
+  };
+  auto issue_a_all = [&](const LTile& t, int kb, int buf) {
+    const unsigned char* src = uni(t.a + 64 * kb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_a(src, t.a_off, lbw(buf), i);
+  };
+  auto issue_b_all = [&](const LTile& t, int kb, int buf) {
+    const unsigned char* w0 = uni(t.w[0] + 2048 * kb);
+    const unsigned char* w1 = uni(t.w[1] + 2048 * kb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_b(w0, w1, lbw(buf), i);
+  };
+
+  // LDS byte offsets of this lane's operand chunks: token row (lane mod 32) of
+  // a block, chunk 2 step + lane / 32; weight block at 1 KB per (block, step)
+  const int ar = lane & 31;
+  const uint32_t a_lane[2] = {static_cast<uint32_t>(64 * ar + 16 * ((0 + (lane >> 5)) ^ lswz(ar))),
+                              static_cast<uint32_t>(64 * ar + 16 * ((2 + (lane >> 5)) ^ lswz(ar)))};
+  // the wave's weight blocks in the tile: gate_up gate 2c, 2c + 1 and up
+  // 4 + 2c, 5 + 2c; down 4c .. 4c + 3
+  auto wblk = [&](int j) { return MODE == kGateUp ? (j < 2 ? 2 * wc + j : 2 + 2 * wc + j) : 4 * wc + j; };
+
+  typedef bf16x8 Frag[8];           // 4 token-block operands, then 4 weight-block operands
+  // operand Q of a step: Q < 4 token block Q, else weight block Q - 4
+  auto read_op = [&](int tb0, int buf, int step, int q, Frag& f) __attribute__((always_inline)) {
+    const unsigned char* s = smem + buf * kLStage;
+    if (q < 4) {
+      // (blocks past the wave's live ones are read too: in bounds, unused)
+      const int tb = q == 0 ? tb0 : 2 * q + wr;
+      f[q] = *reinterpret_cast<const bf16x8*>(s + 2048 * tb + a_lane[step]);
+    } else {
+      f[q] = *reinterpret_cast<const bf16x8*>(s + kLStageA + (2 * wblk(q - 4) + step) * 1024 + 16 * lane);
+    }
+  };
+
+  const int pos = tile_at(0);
+  if (pos < 0) return;
+  LTile cur, nxt;
+  decode(pos, cur);
+  int ring = 0;                      // ring buffer of the current tile's stage 0
+  // stages 0-2 and the token-row half of stage 3 (the weight half of stage
+  // x + 3 is issued in stage x's first step, the token-row half of stage
+  // x + 4 in its second)
+  for (int s = 0; s < kLNS - 1; ++s) {
+    issue_a_all(cur, s, s);
+    issue_b_all(cur, s, s);
+  }
+  issue_a_all(cur, kLNS - 1, kLNS - 1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLLoads + kLLoads / 2));
+  __builtin_amdgcn_s_barrier();
+  Frag f0, f1;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) read_op(cur.tb0, 0, 0, op_order(r), f0);
+
+  bool stored = false;               // the previous tile's stores came between the token-row
+                                     // and the weight halves of this tile's stage 3
+  int round = 0;
+  for (int ti = pos; ti >= 0;) {
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[m][j] = f32x16{0.f};
+    ring = __builtin_amdgcn_readfirstlane(ring);
+    const int nkb = __builtin_amdgcn_readfirstlane(cur.nkb);
+    const int nv = __builtin_amdgcn_readfirstlane(cur.nv);
+    int tn = -1;                     // the next tile (decoded four stages before the end)
+    bool has_next = false;
+
+    // one 16-wide K step over the wave's NV live token blocks; op(k) is the
+    // memory operation issued after the k-th MFMA (k = 0..15; the ones past
+    // a short step's MFMAs follow them), so the loads' and the LDS reads'
+    // issue overlaps the MFMA pipe
+    auto step = [&](const Frag& f, auto nv_tag, auto&& op) __attribute__((always_inline)) {
+      constexpr int NV = decltype(nv_tag)::value;
+#pragma unroll
+      for (int m = 0; m < NV; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[m][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[4 + j], f[m], acc[m][j], 0, 0, 0);
+          op(4 * m + j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+      for (int k = 4 * NV; k < 16; ++k) op(k);
+    };
+
+    // K stage x: step 0 from f0 while reading step 1's operands into f1 and
+    // issuing the weight half of stage x + 3; barrier; step 1 from f1 while
+    // reading stage x + 1's first operands into f0 and issuing the token-row
+    // half of stage x + 4.  Stages past this tile's last are the next tile's;
+    // after the last tile they repeat this tile's first ones (in bounds,
+    // never used), so that every stage issues the same loads and waits.
+    auto stage = [&](int x, auto nv_tag) __attribute__((always_inline)) {
+      const int b0 = (ring + x) & (kLNS - 1);
+      const int b1 = (b0 + 1) & (kLNS - 1);
+      const int b3 = (b0 + kLNS - 1) & (kLNS - 1);
+      const uint32_t l3 = lbw(b3), l0 = lbw(b0);
+      const bool wnx = x + 3 >= nkb;
+      const int wk = wnx ? x + 3 - nkb : x + 3;
+      const unsigned char* w0 = uni((wnx ? nxt.w[0] : cur.w[0]) + 2048 * wk);
+      const unsigned char* w1 = uni((wnx ? nxt.w[1] : cur.w[1]) + 2048 * wk);
+      step(f0, nv_tag, [&](int k) __attribute__((always_inline)) {
+        if ((k & 1) == 0) read_op(cur.tb0, b0, 1, op_order(k >> 1), f1);
+        else if ((k & 3) == 1) issue_b(w0, w1, l3, k >> 2);
+      });
+      if (x == nkb - kLNS) {
+        tn = tile_at(round + 1);
+        has_next = tn >= 0;
+        if (has_next) decode(tn, nxt);
+        else nxt = cur;
+      }
+      // after stage x + 1's last load came both halves of stages x + 2 and
+      // x + 3 and, for stages 1 and 2, the previous tile's stores
+      if (stored && x <= 1) wait_vm<kStores>(2, true);
+      else wait_vm<kStores>(2, false);
+      // every wave's reads of stage x were issued in its first step: done
+      // before the barrier hands the buffer to stage x + 4
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+      __builtin_amdgcn_s_barrier();
+      const bool anx = x + 4 >= nkb;
+      const int ak = anx ? x + 4 - nkb : x + 4;
+      const unsigned char* asrc = uni((anx ? nxt.a : cur.a) + 64 * ak);
+      uint32_t aoff[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) aoff[i] = anx ? nxt.a_off[i] : cur.a_off[i];
+      const int tb0 = x + 1 >= nkb ? nxt.tb0 : cur.tb0;
+      step(f1, nv_tag, [&](int k) __attribute__((always_inline)) {
+        if ((k & 1) == 0) read_op(tb0, b1, 0, op_order(k >> 1), f0);
+        else if ((k & 3) == 1) issue_a(asrc, aoff, l0, k >> 2);
+      });
+    };
+
+    // stages whose loads all come from this tile and whose waits count no
+    // stores: the same work from pointers advanced once per stage
+    auto fast = [&](int x, const unsigned char*& pa, const unsigned char*& pw0, const unsigned char*& pw1,
+                    auto nv_tag) __attribute__((always_inline)) {
+      const int b0 = (ring + x) & (kLNS - 1);
+      const int b1 = (b0 + 1) & (kLNS - 1);
+      const int b3 = (b0 + kLNS - 1) & (kLNS - 1);
+      const uint32_t l3 = lbw(b3), l0 = lbw(b0);
+      step(f0, nv_tag, [&](int k) __attribute__((always_inline)) {
+        if ((k & 1) == 0) read_op(cur.tb0, b0, 1, op_order(k >> 1), f1);
+        else if ((k & 3) == 1) issue_b(pw0, pw1, l3, k >> 2);
+      });
+      wait_vm<kStores>(2, false);
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+      __builtin_amdgcn_s_barrier();
+      step(f1, nv_tag, [&](int k) __attribute__((always_inline)) {
+        if ((k & 1) == 0) read_op(cur.tb0, b1, 0, op_order(k >> 1), f0);
+        else if ((k & 3) == 1) issue_a(pa, cur.a_off, l0, k >> 2);
+      });
+      pa += 64;
+      pw0 += 2048;
+      pw1 += 2048;
+    };
+
+    // the K loop, one copy per count of live token blocks (a ragged last row
+    // block of an expert has fewer): the first two stages (their waits count
+    // the previous tile's stores) and the last four (the next tile's loads)
+    // take the general body, the others the fast one
+    auto k_loop = [&](auto nv_tag) __attribute__((always_inline)) {
+      stage(0, nv_tag);
+      stage(1, nv_tag);
+      const int tail = max(2, nkb - kLNS);
+      const unsigned char* pa = uni(cur.a + 64 * (2 + kLNS));
+      const unsigned char* pw0 = uni(cur.w[0] + 2048 * (2 + kLNS - 1));
+      const unsigned char* pw1 = uni(cur.w[1] + 2048 * (2 + kLNS - 1));
+      for (int x = 2; x < tail; ++x) fast(x, pa, pw0, pw1, nv_tag);
+      for (int x = tail; x < nkb; ++x) stage(x, nv_tag);
+    };
+    switch (nv) {
+      case 4: k_loop(std::integral_constant<int, 4>{}); break;
+      case 3: k_loop(std::integral_constant<int, 3>{}); break;
+      case 2: k_loop(std::integral_constant<int, 2>{}); break;
+      default: k_loop(std::integral_constant<int, 1>{}); break;
+    }
+
+    // ---- epilogue: round, pack and store.  Lane l holds token l mod 32 of a
+    // block and columns 8q + 4 (l / 32) + 0..3 (q = 0..3) of a 32-column
+    // block; one lane-pair swap gives lane l columns 16p + 0..7 and lane l + 32
+    // columns 16p + 8..15.
+    {
+      const LTile& o = cur;
+      uint4 first[kJ][2];            // the wave's first block, rewritten by skipped blocks
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int tb = m == 0 ? o.tb0 : 2 * m + wr;
+        const bool live = m == 0 || m < nv;
+        const int row = min(32 * (live ? tb : o.tb0) + (lane & 31), o.valid - 1);
+        bf16_t* rowp = o.out + static_cast<size_t>(row) * o.ld + 8 * (lane >> 5);
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            uint4 v;
+            if (live) {
+              uint32_t w[2][2];
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const int q = 2 * p + h;
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  if constexpr (MODE == kGateUp) {
+                    const float gv = acc[m][j][4 * q + e], uv = acc[m][j + 2][4 * q + e];
+                    y[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+                  } else {
+                    y[e] = acc[m][j][4 * q + e];
+                  }
+                }
+                w[h][0] = pack_bf16x2(y[0], y[1]);
+                w[h][1] = pack_bf16x2(y[2], y[3]);
+              }
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(w[0][c], w[1][c], false, false);
+                w[0][c] = sw[0];
+                w[1][c] = sw[1];
+              }
+              v = make_uint4(w[0][0], w[0][1], w[1][0], w[1][1]);
+              if (m == 0) first[j][p] = v;
+            } else {
+              v = first[j][p];
+            }
+            *reinterpret_cast<uint4*>(rowp + 32 * j + 16 * p) = v;
+            // a few accumulators at a time
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+    stored = true;
+    ring = (ring + nkb) & (kLNS - 1);
+    ++round;
+    ti = tn;
+    if (has_next) cur = nxt;
+  }
+  // the last tile's trailing loads (repeats of its first stages) land in LDS
+  // before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+}
+
+}  // namespace
+
+bool lds_gemm_fits(int mode, const GemmArgs& a) {
+  const int cols = mode == kGateUp ? kLBN / 2 : kLBN;
+  if (a.E > kGemmMaxE) return false;
+  if (a.E > 0 && (a.K % kLBK != 0 || a.K < kLNS * kLBK || a.N % cols != 0)) return false;
+  if (a.has_shared && (a.Ks % kLBK != 0 || a.Ks < kLNS * kLBK || a.Ns % cols != 0)) return false;
+  return true;
+}
+
+hipError_t launch_lds_gemm(int mode, const GemmArgs& a, hipStream_t st) {
+  if (mode == kGateUp)
+    lds_gemm_kernel<kGateUp><<<persistent_grid(), kLThreads, 0, st>>>(a);
+  else
+    lds_gemm_kernel<kDown><<<persistent_grid(), kLThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -45,7 +45,9 @@ def _sig(a: float) -> float:
     return 1.0 / (1.0 + math.exp(-a))
 
 
-def _swiglu_loops(xv: Sequence[float], wgu, wd) -> List[float]:
+def swiglu_hidden_loops(xv: Sequence[float], wgu) -> List[float]:
+    """h_f = silu(g_f) * u_f with g_f = <W_gate row f, x>, u_f = <W_up row f, x>
+    (rows 0..F-1 of wgu are the gate projection, F..2F-1 the up projection)."""
     F = len(wgu) // 2
     D = len(xv)
     h = []
@@ -56,7 +58,12 @@ def _swiglu_loops(xv: Sequence[float], wgu, wd) -> List[float]:
             g += float(wgu[f][d]) * xv[d]
             u += float(wgu[F + f][d]) * xv[d]
         h.append(g * _sig(g) * u)
-    return [sum(float(wd[d][f]) * h[f] for f in range(F)) for d in range(len(wd))]
+    return h
+
+
+def _swiglu_loops(xv: Sequence[float], wgu, wd) -> List[float]:
+    h = swiglu_hidden_loops(xv, wgu)
+    return [sum(float(wd[d][f]) * h[f] for f in range(len(h))) for d in range(len(wd))]
 
 
 def _as64(a):

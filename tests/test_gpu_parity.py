@@ -73,6 +73,31 @@ def test_small_bf16_full_parity_ragged():
     full_parity(SMALL_BF16)
 
 
+# Shapes with several hundred rows per expert take the LDS-tiled grouped GEMMs
+# (256 x 256 tiles, ragged last row tiles of each expert, shared expert first)
+LDS_TILED = [
+    configs.variant(SMALL_BF16, name="lds_tiled_t1600_e4_k2", T=1600, D=512, E=4, k=2, F=256, Fs=256,
+                    seed=31),
+    configs.variant(SMALL_BF16, name="lds_tiled_t2000_e8_k4_noshared", T=2000, D=256, E=8, k=4, F=512,
+                    Fs=0, seed=32),
+    configs.variant(SMALL_BF16, name="lds_tiled_t1700_e2_k1", T=1700, D=768, E=2, k=1, F=256, Fs=512,
+                    seed=33),
+]
+
+
+@pytest.mark.parametrize("s", LDS_TILED, ids=lambda s: s.name)
+@pytest.mark.parametrize("gather", [False, True])
+def test_lds_tiled_gemm_full_parity(s, gather):
+    inp, b, r = full_parity(s, gather=gather)
+    # every h and y_perm row of every expert, against the oracle's expert rows
+    h = b.h[: s.S * s.F].view(s.S, s.F)
+    for e in range(s.E):
+        h_ref, y_ref = O.expert_rows(inp, r, e)
+        lo, hi = int(r.offsets[e]), int(r.offsets[e + 1])
+        assert_close_rel(to_f64(h[lo:hi]), h_ref, out_tolerance(s), f"h of expert {e}")
+        assert_close_rel(to_f64(b.y_perm[lo:hi]), y_ref, out_tolerance(s), f"y_perm of expert {e}")
+
+
 @pytest.mark.parametrize("seed", [21, 22, 23])
 def test_small_bf16_full_parity_other_seeds(seed):
     # other inputs and weights of the same ragged shape

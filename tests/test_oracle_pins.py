@@ -20,7 +20,8 @@ import numpy as np
 import pytest
 
 from oracle import moe_oracle as O
-from tests.helpers import ArrayInputs, brute_force_layer, random_inputs, rank_count_select
+from tests.helpers import (ArrayInputs, _as64, _swiglu_loops, brute_force_layer, random_inputs,
+                           rank_count_select, swiglu_hidden_loops)
 from mixture_experts_transformer_moe_amd import configs, inputs as gen
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -63,6 +64,51 @@ def _check_brute(case, oracle=O, alpha=2.5):
 @pytest.mark.parametrize("case", BRUTE_CASES)
 def test_oracle_matches_brute_force(case):
     assert _check_brute(case)
+
+
+def _check_expert_rows(oracle=O) -> bool:
+    """expert_rows (the per-expert h and y rows in expert order that the
+    full-size GPU checks compare against) equals the loop brute force row by
+    row: h_f = silu(<W_g row f, x>) * <W_u row f, x>, y = W_d h, for every
+    expert's whole segment and for a subset of positions inside it."""
+    rng = np.random.default_rng(321)
+    T, D, E, F, k = 9, 5, 4, 3, 2
+    inp = random_inputs(rng, T, D, E, F, 0)
+    r = oracle.route(oracle.router_logits(inp.x, inp.w_router, None), k)
+    x = _as64(inp.x).tolist()
+    for e in range(E):
+        wgu, wd = (_as64(a).tolist() for a in inp.expert(e))
+        n = int(r.offsets[e + 1] - r.offsets[e])
+        for rows in (None, np.arange(n)[::-2]):
+            h, y = oracle.expert_rows(inp, r, e, rows)
+            pos = np.arange(n) if rows is None else rows
+            if h.shape != (len(pos), F) or y.shape != (len(pos), D):
+                return False
+            for i, p in enumerate(pos):
+                t = int(r.sorted_token[int(r.offsets[e]) + int(p)])
+                h_ref = swiglu_hidden_loops(x[t], wgu)
+                y_ref = _swiglu_loops(x[t], wgu, wd)
+                if not np.allclose(h[i], h_ref, rtol=1e-12, atol=1e-14):
+                    return False
+                if not np.allclose(y[i], y_ref, rtol=1e-12, atol=1e-14):
+                    return False
+    return True
+
+
+def test_expert_rows_matches_brute_force():
+    assert _check_expert_rows()
+
+
+def test_expert_rows_equals_swiglu_expert_on_each_segment():
+    rng = np.random.default_rng(7)
+    inp = random_inputs(rng, 16, 6, 5, 4, 3)
+    r = O.route(O.router_logits(inp.x, inp.w_router, None), 3)
+    for e in range(5):
+        lo, hi = int(r.offsets[e]), int(r.offsets[e + 1])
+        _, y = O.expert_rows(inp, r, e)
+        a, b = inp.expert(e)
+        ref = O.swiglu_expert(O.widen(np.asarray(inp.x)[r.sorted_token[lo:hi]]), O.widen(a), O.widen(b))
+        np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-15)
 
 
 def test_brute_force_on_bf16_storage():
@@ -379,6 +425,8 @@ def _battery(oracle) -> bool:
         y = oracle.swiglu_expert(np.array([[1.0]]), np.array([[LN3], [2.0]]), np.array([[1.0]]))
         if abs(y[0, 0] - 1.5 * LN3) > 1e-12:
             return False
+        if not _check_expert_rows(oracle):
+            return False
     except Exception:
         return False
     return True
@@ -416,6 +464,27 @@ def _mut_scale_shared(inputs, xrows64):
     return 2.5 * O.swiglu_expert(xrows64, O.widen(sh[0]), O.widen(sh[1]))
 
 
+def _mut_expert_rows_swapped(inputs, routing, e, rows=None):
+    lo, hi = int(routing.offsets[e]), int(routing.offsets[e + 1])
+    pos = np.arange(lo, hi) if rows is None else lo + np.asarray(rows, dtype=np.int64)
+    wgu, wd = (O.widen(a) for a in inputs.expert(e))
+    xr = O.widen(np.asarray(inputs.x)[routing.sorted_token[pos]])
+    F = wgu.shape[0] // 2
+    h = O.silu(xr @ wgu[F:].T) * (xr @ wgu[:F].T)
+    return h, h @ wd.T
+
+
+def _mut_expert_rows_unsorted(inputs, routing, e, rows=None):
+    # rows taken in token order instead of the expert order
+    lo, hi = int(routing.offsets[e]), int(routing.offsets[e + 1])
+    pos = np.arange(lo, hi) if rows is None else lo + np.asarray(rows, dtype=np.int64)
+    wgu, wd = (O.widen(a) for a in inputs.expert(e))
+    xr = O.widen(np.asarray(inputs.x)[pos % np.asarray(inputs.x).shape[0]])
+    F = wgu.shape[0] // 2
+    h = O.silu(xr @ wgu[:F].T) * (xr @ wgu[F:].T)
+    return h, h @ wd.T
+
+
 def _mut_relu_gate(xrows, wgu, wd):
     F = wgu.shape[0] // 2
     return (np.maximum(xrows @ wgu[:F].T, 0) * (xrows @ wgu[F:].T)) @ wd.T
@@ -429,6 +498,8 @@ def _mut_relu_gate(xrows, wgu, wd):
     ("ties to higher index", "select_topk", _mut_high_index_ties),
     ("router bias dropped", "router_logits", _mut_drop_bias),
     ("alpha on the shared expert", "shared_output", _mut_scale_shared),
+    ("expert_rows: silu on the up branch", "expert_rows", _mut_expert_rows_swapped),
+    ("expert_rows: rows not in expert order", "expert_rows", _mut_expert_rows_unsorted),
 ])
 def test_planted_mistakes_are_caught(monkeypatch, name, attr, mutant):
     assert _battery(O)
