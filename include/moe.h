@@ -134,6 +134,25 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, 
                 int32_t* offsets, int32_t* sorted_token, int32_t* slot_of, void* x_perm,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_permute for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and outputs, with the per-block histograms in a
+ * device-resident array of the library instead of a caller workspace.
+ *   - the array holds 1 MiB per GPU (kept until the process ends), enough for
+ *     moe_workspace_bytes(shape) <= 1 MiB, i.e. ceil(T / 256) * E * 4 bytes
+ *     (T <= 262144 tokens at E = 256); larger shapes return
+ *     MOE_ERR_UNSUPPORTED before anything is launched;
+ *   - nothing is allocated or freed; the array's address on the current device
+ *     is looked up once per device (MOE_ERR_HIP if that fails);
+ *   - every call on one GPU shares that GPU's array: calls that overlap on one
+ *     GPU (other streams, other threads) race and must be ordered by the caller;
+ *     no part of the array needs to start at zero (each call writes what it
+ *     reads).
+ * Arguments as moe_permute, without workspace and workspace_bytes. */
+int moe_permute_static(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_token, int32_t* slot_of, void* x_perm,
+                       void* stream);
+
 /* Repack weight matrices into MFMA fragment order, the layout every weight
  * argument of moe_grouped_gate_up / moe_grouped_down / moe_grouped_ffn takes
  * (a one-time pass when weights are loaded; the pages' experts are the

@@ -31,7 +31,7 @@ EXPORTS = ("moe_version", "moe_status_string", "moe_last_error", "moe_workspace_
            "moe_route_masked", "moe_train_workspace_bytes", "moe_packed_transposed_bytes",
            "moe_pack_weights_transposed", "moe_load_stats", "moe_grouped_gate_up_train",
            "moe_combine_backward", "moe_grouped_backward_h", "moe_grouped_backward_x",
-           "moe_weight_grads", "moe_bias_grad", "moe_shared_ffn")
+           "moe_weight_grads", "moe_bias_grad", "moe_shared_ffn", "moe_permute_static")
 
 
 class moe_shape(ctypes.Structure):
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P]
         L.moe_permute.restype = ctypes.c_int
         L.moe_permute.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_permute_static.restype = ctypes.c_int
+        L.moe_permute_static.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_pack_weights.restype = ctypes.c_int
         L.moe_pack_weights.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, _P]
@@ -167,6 +169,12 @@ def moe_permute(shape, topk_idx, x, counts, offsets, sorted_token, slot_of, x_pe
     _check(lib().moe_permute(ctypes.byref(shape), _ptr(topk_idx), _ptr(x), _ptr(counts),
                              _ptr(offsets), _ptr(sorted_token), _ptr(slot_of), _ptr(x_perm),
                              _ptr(workspace), nbytes, _stream(stream)), "moe_permute")
+
+
+def moe_permute_static(shape, topk_idx, x, counts, offsets, sorted_token, slot_of, x_perm, stream=None):
+    _check(lib().moe_permute_static(ctypes.byref(shape), _ptr(topk_idx), _ptr(x), _ptr(counts),
+                                    _ptr(offsets), _ptr(sorted_token), _ptr(slot_of), _ptr(x_perm),
+                                    _stream(stream)), "moe_permute_static")
 
 
 def moe_pack_weights(w, w_packed, count, rows, cols, dtype, stream=None):

@@ -150,6 +150,30 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, 
                                       x_perm, workspace, as_stream(stream)));
 }
 
+int moe_permute_static(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_token, int32_t* slot_of, void* x_perm,
+                       void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (shape->T == 0) return ok();
+  NEED_PTR(topk_idx);
+  NEED_PTR(counts);
+  NEED_PTR(offsets);
+  NEED_PTR(sorted_token);
+  NEED_PTR(slot_of);
+  OPT_PTR(x_perm);
+  if (x_perm) NEED_PTR(x);
+  const size_t need = moe::permute_workspace_bytes(*shape);
+  if (need > moe::static_scratch_bytes())
+    return fail(MOE_ERR_UNSUPPORTED, "moe_permute_static: %zu bytes of scratch needed, %zu available "
+                "(T = %d, E = %d); use moe_permute with a workspace", need, moe::static_scratch_bytes(),
+                shape->T, shape->E);
+  void* scratch = nullptr;
+  if (hipError_t e = moe::static_scratch(&scratch))
+    return fail(MOE_ERR_HIP, "moe_permute_static: scratch address lookup failed: %s", hipGetErrorString(e));
+  return launched(moe::launch_permute(*shape, topk_idx, x, counts, offsets, sorted_token, slot_of,
+                                      x_perm, scratch, as_stream(stream)));
+}
+
 int moe_grouped_gate_up(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
                         const void* x, const int32_t* offsets, const void* w_gate_up,
                         const void* ws_gate_up, void* h, void* stream) {

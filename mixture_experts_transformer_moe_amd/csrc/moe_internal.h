@@ -45,6 +45,10 @@ hipError_t launch_route_f32(const moe_shape& s, const float* x, const float* wr,
                             float* w, hipStream_t st);
 
 size_t permute_workspace_bytes(const moe_shape& s);
+// the device-resident scratch of moe_permute_static: its size, and its address
+// on the current device (looked up once per device)
+size_t static_scratch_bytes();
+hipError_t static_scratch(void** out);
 hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_token, int32_t* slot_of,
                           void* x_perm, void* workspace, hipStream_t st);

@@ -18,6 +18,9 @@
 // A negative expert index marks a slot that is not routed (a padding token):
 // it takes no position, its slot_of is -1, and offsets[E] is the number of
 // routed slots.
+#include <atomic>
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -218,6 +221,41 @@ __global__ __launch_bounds__(256) void perm_gather_kernel(const u32x4* __restric
 }
 
 }  // namespace
+
+// Scratch of the entry point that allocates nothing (moe_permute_static): the
+// per-block expert histograms in a device array of fixed size.  Each GPU the
+// library runs on holds its own copy until the process ends; its address is
+// looked up once per device with that device current and kept per device (the
+// array's name is a host-side stand-in, never an address to hand a kernel).
+// Nothing in it needs clearing: the histogram kernel writes every entry the
+// scatter kernel then reads.
+constexpr size_t kStaticScratchBytes = size_t{1} << 20;
+static __device__ __align__(256) int32_t scratch[kStaticScratchBytes / sizeof(int32_t)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+size_t static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 size_t permute_workspace_bytes(const moe_shape& s) {
   const size_t nb = (static_cast<size_t>(s.T) + kTB - 1) / kTB;

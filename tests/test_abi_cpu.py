@@ -99,6 +99,24 @@ def test_workspace_checks(L):
     assert st == binding.MOE_ERR_WORKSPACE
 
 
+def test_permute_static_checks_before_launch(L):
+    # null outputs are rejected like moe_permute's
+    s = _shape()
+    p = ctypes.c_void_p(4096)
+    assert L.moe_permute_static(ctypes.byref(s), p, p, None, p, p, p, None, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    # its device-resident scratch holds 1 MiB of histograms: ceil(T / 256) * E * 4
+    # bytes; one more 256-token block at E = 256 is refused with a clear error
+    big = _shape(T=1024 * 256 + 1, E=256, k=1)
+    assert L.moe_workspace_bytes(ctypes.byref(big)) > 1 << 20
+    st = L.moe_permute_static(ctypes.byref(big), p, p, p, p, p, p, None, None)
+    assert st == binding.MOE_ERR_UNSUPPORTED
+    assert b"scratch" in L.moe_last_error()
+    # an empty batch is a no-op, as for every entry point
+    assert L.moe_permute_static(ctypes.byref(_shape(T=0)), None, None, None, None, None, None, None,
+                                None) == binding.MOE_OK
+
+
 def test_empty_batch_is_a_no_op(L):
     s = _shape(T=0)
     assert _route(L, s, ptr=0) == binding.MOE_OK
