@@ -9,12 +9,18 @@ then K timed steps between two device synchronisations.  Prints one JSON line:
 tokens/s of the layer, plus
 
   roofline      the dominant kernel (the gate/up grouped GEMM with its SwiGLU
-                epilogue): algorithmic bytes (or FLOPs) per launch divided by its
-                average duration, measured with HIP events recorded on the stream
-                it runs on around its launches in every fourth timed step,
-                against the MI355X peak that bounds it;
+                epilogue): algorithmic bytes (or FLOPs) per launch divided by the
+                median duration of its launches, measured with HIP events recorded
+                on the stream it runs on, in an untimed pass right after the timed
+                steps, against the MI355X peak that bounds it;
+  grouped_ffn   the two grouped GEMMs together (gate/up + down), priced the same
+                way: MFMA share of the bf16 peak, and HBM share for the bytes;
   cpu_baseline  the CPU oracle (fp64 NumPy, self-contained routing) timed on the
                 host cores on the same workload.
+
+Before the W warmup steps an untimed settle phase runs steps until at least
+40 of them and 100 ms of device time have passed (the clocks take some tens of
+milliseconds of load to settle); its length is reported as `settle`.
 
 With --train, one step is the training pass instead (forward keeping the
 activations the backward needs, then every gradient), on the padded XS.2
@@ -52,7 +58,8 @@ PEAK_F32_TFLOPS = 157.3
 # the traffic is reported as null until the counters are taken again.
 FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
-GEMM_SOURCES = ("grouped_gemm.hip", "mma_stream.h", "lds_dma.h", "moe_internal.h")
+GEMM_SOURCES = ("grouped_gemm.hip", "grouped_gemm_lds.hip", "grouped_gemm.h", "mma_stream.h", "lds_dma.h",
+                "moe_internal.h")
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
     "xs2_bf16_t4096_d2048": (662779.1, 37054.2,
@@ -105,6 +112,38 @@ def gate_up_work(s: configs.MoEShape, n_touched: int, fp8: bool = False, shared:
     a = (s.S + (s.T if s.Fs else 0)) * s.D * el
     h = (s.S * s.F + s.T * s.Fs) * el
     return flops, float(w + a + h)
+
+
+def down_work(s: configs.MoEShape, n_touched: int, fp8: bool = False, shared: bool = True):
+    """Algorithmic FLOPs and HBM bytes of one down grouped-GEMM launch:
+    weights of the touched routed experts (D x F each) + shared weights (1 byte
+    per weight and a 4-byte scale per row with FP8 weights) + h rows read
+    ((k*T*F + T*Fs) elements) + y rows written ((k*T + T) rows of width D)."""
+    if not shared:
+        s = configs.variant(s, Fs=0)
+    el = 2 if s.dtype == "bf16" else 4
+    flops = 2.0 * s.S * s.D * s.F + 2.0 * s.T * s.D * s.Fs
+    if fp8:
+        w = (n_touched * s.D + (s.D if s.Fs else 0)) * 4 + (n_touched * s.D * s.F + s.D * s.Fs)
+    else:
+        w = (n_touched * s.D * s.F + s.D * s.Fs) * el
+    h = (s.S * s.F + s.T * s.Fs) * el
+    y = (s.S + (s.T if s.Fs else 0)) * s.D * el
+    return flops, float(w + h + y)
+
+
+def settle(step, min_steps: int = 40, min_ms: float = 100.0):
+    """Untimed steps until at least min_steps of them and min_ms of wall time
+    (with the device synchronised after each step) have passed."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_steps or (time.perf_counter() - t0) * 1e3 < min_ms:
+        step()
+        torch.cuda.synchronize()
+        n += 1
+    return {"steps": n, "ms": round((time.perf_counter() - t0) * 1e3, 1)}
 
 
 def cpu_oracle_baseline(s, inp_host, target_s: float = 12.0, fp8: bool = False, gpu_topk=None):
@@ -283,6 +322,7 @@ def train_main(args):
             ev[1].record(stream)
         binding.moe_bias_grad(c, b.dz, b.dbias, b.train_ws, stream)
 
+    settled = settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -312,7 +352,7 @@ def train_main(args):
     line = {
         "metric": "MoE-layer training tokens/s (forward + backward) at 1 MI355X",
         "value": round(s.T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "steps": args.steps, "warmup": args.warmup, "settle": settled, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.dtype,
         "data": "synthetic",
         "config": {"workload": s.name, "tokens": s.T, "routed_tokens": routed_rows // s.k,
@@ -329,9 +369,9 @@ def train_main(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    # the clocks take some tens of milliseconds of load to settle
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
+    # (an untimed settle phase runs before these: at least 40 steps and 100 ms)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=configs.BENCH_WORKLOAD, choices=sorted(configs.WORKLOADS))
     ap.add_argument("--split-shared", action="store_true",
                     help="run the shared expert on a second stream beside the router and the "
@@ -415,12 +455,16 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         mark(3)
+        if ev is not None:
+            ev[2].record(stream)
         if w.fp8:
             binding.moe_grouped_down_fp8(c, b.h, b.offsets, w.w_down, w.w_down_scale, w.ws_down,
                                          w.ws_down_scale, b.y_perm, b.y_shared, stream)
         else:
             binding.moe_grouped_down(c, b.h, b.offsets, w.w_down, None if split else w.ws_down,
                                      b.y_perm, b.y_shared, stream)
+        if ev is not None:
+            ev[3].record(stream)
         mark(4)
         if split:
             stream.wait_event(ev_shared)
@@ -429,22 +473,24 @@ def main():
         if split:
             ev_done.record(stream)
 
+    settled = settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # the gate/up launch of every EV_EVERY-th timed step is bracketed by two
-    # events on its stream (each event costs the stream a few microseconds)
-    timed = list(range(0, args.steps, EV_EVERY))
-    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for i in timed}
+    # every timed step brackets its gate/up and down launches with HIP events
+    # on their stream (each event costs the stream a few microseconds)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs.get(i))
+        step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    gate_up_ms = float(np.mean([a.elapsed_time(z) for a, z in evs.values()]))
+    gu_times = [e[0].elapsed_time(e[1]) for e in evs]
+    dn_times = [e[2].elapsed_time(e[3]) for e in evs]
+    gate_up_ms = float(np.mean(gu_times))
+    down_ms = float(np.mean(dn_times))
 
     # per-call medians (untimed pass after the timed steps: events between the
     # calls on the layer's stream, 20 steps after 5 warmup ones)
@@ -465,6 +511,7 @@ def main():
     counts = b.counts.cpu().numpy()
     n_touched = int(np.count_nonzero(counts))
     flops, nbytes = gate_up_work(s, n_touched, args.fp8_weights, shared=not split)
+    dflops, dbytes = down_work(s, n_touched, args.fp8_weights, shared=not split)
     intensity = flops / nbytes
     peak_flops = PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_F32_TFLOPS
     ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -478,12 +525,22 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4)}
     traffic = None if (args.fp8_weights or split) else measured_traffic(s.name)
     kname = ("grouped_gemm_kernel<gate_up, FP8 weights> (moe_grouped_gate_up_fp8)" if args.fp8_weights
-             else "grouped_gemm_kernel<gate_up> (moe_grouped_gate_up, routed experts only)" if split
-             else "grouped_gemm_kernel<gate_up> (moe_grouped_gate_up)")
+             else "gate/up grouped GEMM (moe_grouped_gate_up, routed experts only)" if split
+             else "gate/up grouped GEMM (moe_grouped_gate_up)")
     roof.update({"traffic": traffic, "kernel": kname,
-                 "kernel_ms": round(gate_up_ms, 4), "algorithmic_bytes": nbytes,
+                 "kernel_ms": round(gate_up_ms, 4), "kernel_ms_median": round(float(np.median(gu_times)), 4),
+                 "launches": len(gu_times), "algorithmic_bytes": nbytes,
                  "algorithmic_flops": flops,
                  "mfma_tflops": round(flops / (gate_up_ms * 1e-3) / 1e12, 1)})
+    # the grouped FFN (a6 + a7) as a whole, from the same timed launches
+    ffn_ms = gate_up_ms + down_ms
+    ffn = {"gate_up_ms": round(gate_up_ms, 4), "down_ms": round(down_ms, 4),
+           "flops": flops + dflops, "bytes": nbytes + dbytes,
+           "mfma_tflops": round((flops + dflops) / (ffn_ms * 1e-3) / 1e12, 1),
+           "mfma_frac": round((flops + dflops) / (ffn_ms * 1e-3) / 1e12 / peak_flops, 4),
+           "hbm_gbs": round((nbytes + dbytes) / (ffn_ms * 1e-3) / 1e9, 1),
+           "hbm_frac": round((nbytes + dbytes) / (ffn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "graded_on": "mfma" if intensity >= ridge else "hbm"}
 
     ms = elapsed * 1e3 / args.steps
     tokens_per_s = s.T * args.steps / elapsed
@@ -493,7 +550,7 @@ def main():
         cpu = cpu_oracle_baseline(s, host, fp8=args.fp8_weights, gpu_topk=b.topk_idx.cpu().numpy())
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "steps": args.steps, "warmup": args.warmup, "settle": settled, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.dtype,
         "data": "synthetic",
         "config": {"workload": s.name, "tokens": s.T, "d_model": s.D, "experts": s.E,
@@ -505,7 +562,7 @@ def main():
         "experts_touched": n_touched, "rows_per_expert_max": int(counts.max()),
         "calls_median_ms": calls_ms,
         "tokens_per_s_from_call_medians": round(s.T / (sum(calls_ms.values()) * 1e-3), 1),
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "grouped_ffn": ffn, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

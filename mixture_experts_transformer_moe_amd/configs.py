@@ -99,8 +99,9 @@ WORKLOADS: Dict[str, MoEShape] = {s.name: s for s in
                                   (TINY_F32, XS2_T4096, M1_T8192, DECODE_SKEW_T32,
                                    PREFILL_OUTLIER_T32768, M1_TOP16_T8192, XS2_TRAIN_T4096)}
 
-# The single-GPU benchmark workload: the XS.2-shaped layer.
-BENCH_WORKLOAD = XS2_T4096.name
+# The single-GPU benchmark workload: the largest single-GPU configuration, the
+# long prefill chunk (32768 tokens at the XS.2 widths: 1.89 TFLOP per pass).
+BENCH_WORKLOAD = PREFILL_OUTLIER_T32768.name
 
 
 def get(name: str) -> MoEShape:

@@ -87,3 +87,26 @@ def test_cpu_training_baseline_runs_on_a_small_padded_batch(bench):
     res = bench.cpu_train_baseline(s, host, I.token_mask(s), I.dout_encoded(s), target_s=0.2)
     assert res["kind"] == "oracle" and res["unit"] == "tokens/s" and res["value"] > 0
     assert res["cores"] >= 1 and "training oracle" in res["sample"]
+
+
+def test_down_work_counts_each_term_once(bench):
+    s = configs.PREFILL_OUTLIER_T32768
+    flops, nbytes = bench.down_work(s, n_touched=256)
+    # y = h W_d^T: m x F by F x D per expert, 2 m F D flops
+    assert flops == 2 * (s.T * s.k) * s.F * s.D + 2 * s.T * s.Fs * s.D
+    weights = (256 * s.D * s.F + s.D * s.Fs) * 2
+    h_in = (s.T * s.k * s.F + s.T * s.Fs) * 2
+    y_out = (s.T * s.k + s.T) * s.D * 2
+    assert nbytes == weights + h_in + y_out
+    f0, b0 = bench.down_work(s, n_touched=256, shared=False)
+    assert f0 == 2 * (s.T * s.k) * s.F * s.D
+    assert b0 == 256 * s.D * s.F * 2 + s.T * s.k * s.F * 2 + s.T * s.k * s.D * 2
+
+
+def test_bench_workload_is_the_largest_single_gpu_config():
+    # the headline runs on the configured workload with the most work per pass
+    # (the five layer configurations: tiny fp32, XS.2, M.1, decode, long prefill)
+    five = [configs.TINY_F32, configs.XS2_T4096, configs.M1_T8192, configs.DECODE_SKEW_T32,
+            configs.PREFILL_OUTLIER_T32768]
+    largest = max(five, key=lambda w: w.flops())
+    assert configs.BENCH_WORKLOAD == largest.name == configs.PREFILL_OUTLIER_T32768.name
