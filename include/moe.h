@@ -227,7 +227,20 @@ int moe_grouped_down(const moe_shape* shape, const void* h, const int32_t* offse
 int moe_shared_ffn(const moe_shape* shape, const void* x, const void* ws_gate_up,
                    const void* ws_down, void* h_shared, void* y_shared, void* stream);
 
-/* moe_grouped_gate_up followed by moe_grouped_down on the same stream. */
+/* moe_grouped_gate_up followed by moe_grouped_down on the same stream.
+ * The expert weights this takes are NOT row-major [E, 2F, D] / [E, D, F]: they
+ * are the output of moe_pack_weights (the same bytes permuted into MFMA operand
+ * order, a one-time step when weights are loaded, into a buffer the caller owns
+ * and reuses for every call).  Row-major weights have the same size and cannot
+ * be told apart here: passing them gives wrong results, not an error.  The
+ * grouped GEMMs read every 32-row x 16-column operand block of a weight matrix
+ * as one contiguous 1 KB load; packing per call would add a full read and
+ * write of the expert weights (1.6-6.4 GB at the configured widths) to every
+ * pass.  They need no workspace (the tile table is built on the device from
+ * offsets), and with x_perm NULL they read x through sorted_token instead of a
+ * materialised copy.  bf16 widths D, F, Fs must be multiples of 256 (whole
+ * weight-prefetch rounds of the reduction, 128- and 256-wide output tiles):
+ * other widths return MOE_ERR_UNSUPPORTED. */
 int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* sorted_token,
                     const void* x, const int32_t* offsets, const void* w_gate_up,
                     const void* w_down, const void* ws_gate_up, const void* ws_down, void* h,

@@ -402,11 +402,15 @@ hipError_t launch_tiles(const GemmArgs& a, int mean_rows, hipStream_t st) {
   // steps) of FP8 ones
   constexpr int P = W8 ? 8 : 16;
   const int wide = MODE == kGateUp ? 256 : 512;            // output columns of an NB = 4 tile
-  // From ~768 rows per expert the LDS-tiled kernel's 256-row tiles hold most
-  // of an expert's rows in full tiles (measured faster at 1024 rows per expert,
-  // slower at 256 and 512, where the short last row tile of each expert
-  // streams its weights for few rows)
-  if (!W8 && mean_rows >= 768 && lds_gemm_fits(MODE, a)) return launch_lds_gemm(MODE, a, st);
+  // The LDS-tiled kernel (256 x 256 tiles, both operands through LDS) beats
+  // the weight-streaming tiles below once most of an expert's rows sit in full
+  // 256-row tiles. Measured: the down projection (K = F) from 256 rows per
+  // expert on (7% faster at 256 and at 512, 11% at 1024); the gate/up
+  // projection (K = D) only at 1024 (11% faster; 1-2% slower at 256 and 512,
+  // where the short last row tile of each expert streams a full 256 x D slice
+  // of weights for few rows)
+  const int lds_from = MODE == kDown ? 256 : 768;
+  if (!W8 && mean_rows >= lds_from && lds_gemm_fits(MODE, a)) return launch_lds_gemm(MODE, a, st);
   if (mean_rows >= 192 && a.N % wide == 0 && (!a.has_shared || a.Ns % wide == 0))
     grouped_gemm_kernel<MODE, 96, 4, 8, W8><<<persistent_grid(), kThreads, 0, st>>>(a);
   else if (mean_rows >= 96)

@@ -114,6 +114,9 @@ struct LTile {
   bf16_t* out;                 // output element (tile row r, column c of the wave) at out + r * ld + c
   int ld;
   int valid;                   // rows of the tile
+  int gathered;                // token rows gathered through the expert order
+  const int32_t* ids;          // gathered: the tile's token ids (rows past valid - 1 repeat its last)
+  int K;                       // reduction length (elements)
 };
 
 // A pointer that is the same in every lane, made visibly so (SGPRs).
@@ -143,7 +146,8 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kLNS * kLStage];
   __shared__ int tile_end[kGemmMaxE + 1];
   __shared__ int row_base[kGemmMaxE + 1];
-  static_assert(kLNS * kLStage + 2 * (kGemmMaxE + 1) * 4 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(256))) int32_t ids_lds[4][64];   // next tile's token ids, per wave
+  static_assert(kLNS * kLStage + 2 * (kGemmMaxE + 1) * 4 + 4 * 64 * 4 <= 160 * 1024, "LDS");
   constexpr int kOutCols = MODE == kGateUp ? kLBN / 2 : kLBN;    // output columns per tile
   constexpr int kJ = MODE == kGateUp ? 2 : 4;                    // output blocks of 32 per wave
   constexpr int kStores = 4 * kJ * 2;                            // 16-byte stores per wave and tile
@@ -234,18 +238,12 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
     // lane l row 64 wave + 16 i + l / 4, LDS slot l % 4 = logical chunk
     // (l % 4) ^ lswz(row); rows past the tile's last repeat it
     const bool gathered = !shared && g.gather != nullptr;
+    t.gathered = gathered;
+    t.K = K;
+    t.ids = gathered ? uni(g.gather + rb + m0) : nullptr;
     if (gathered) {
-      // token ids by vector loads (one per lane and load): the compiler waits
-      // for them with everything in flight, once per tile
-      const int32_t* gt = g.gather + rb + m0;
+      // token ids arrive later through LDS (ids_issue / ids_offsets)
       t.a = uni(reinterpret_cast<const unsigned char*>(g.a_routed));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 64 * wave + 16 * i + (ln >> 2);
-        const int tok = min(max(gt[min(row, valid - 1)], 0), g.T - 1);
-        const int c = (ln & 3) ^ lswz(row);
-        t.a_off[i] = (static_cast<uint32_t>(tok) * static_cast<uint32_t>(K) + 8u * c) * 2u;
-      }
     } else {
       t.a = uni(reinterpret_cast<const unsigned char*>(shared ? g.a_shared + static_cast<size_t>(m0) * K
                                                               : g.a_routed + static_cast<size_t>(rb + m0) * K));
@@ -270,8 +268,8 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
     }
     // output: the wave's columns
     const int col0 = n0 + (MODE == kGateUp ? 64 : 128) * wc;
-    t.out = (shared ? g.out_shared + static_cast<size_t>(m0) * Nout
-                    : g.out_routed + static_cast<size_t>(rb + m0) * Nout) + col0;
+    t.out = const_cast<bf16_t*>(uni((shared ? g.out_shared + static_cast<size_t>(m0) * Nout
+                                            : g.out_routed + static_cast<size_t>(rb + m0) * Nout) + col0));
     t.ld = Nout;
   };
 
@@ -312,6 +310,34 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
     for (int i = 0; i < 4; ++i) issue_b(w0, w1, lbw(buf), i);
   };
 
+  // Token ids of a gathered tile: one direct load of 4 bytes per lane puts the
+  // ids of the wave's 64 rows (64 wave + l, clamped to the tile's last row)
+  // into ids_lds[wave]; a tile that gathers nothing (or no tile) loads 256
+  // harmless bytes of `dummy` instead, so every tile issues exactly one.
+  const uint32_t ids_l = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds_addr(&ids_lds[wave][0])));
+  auto ids_issue = [&](const LTile& t, bool real, const unsigned char* dummy) __attribute__((always_inline)) {
+    const bool gath = real && t.gathered;
+    const unsigned char* base = uni(gath ? reinterpret_cast<const unsigned char*>(t.ids) : dummy);
+    const uint32_t voff = gath ? static_cast<uint32_t>(min(64 * wave + lane, t.valid - 1)) * 4u
+                               : static_cast<uint32_t>(lane) * 4u;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(ids_l)
+                 : "memory", "m0");
+  };
+  // the row offsets of a gathered tile from its ids in LDS (once its load
+  // has landed): load i, lane l reads row 64 wave + 16 i + l / 4
+  auto ids_offsets = [&](LTile& t) __attribute__((always_inline)) {
+    if (!t.gathered) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 64 * wave + 16 * i + (lane >> 2);
+      const int tok = min(max(ids_lds[wave][16 * i + (lane >> 2)], 0), g.T - 1);
+      const int c = (lane & 3) ^ lswz(row);
+      t.a_off[i] = (static_cast<uint32_t>(tok) * static_cast<uint32_t>(t.K) + 8u * c) * 2u;
+    }
+  };
+
   // LDS byte offsets of this lane's operand chunks: token row (lane mod 32) of
   // a block, chunk 2 step + lane / 32; weight block at 1 KB per (block, step)
   const int ar = lane & 31;
@@ -338,6 +364,9 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
   if (pos < 0) return;
   LTile cur, nxt;
   decode(pos, cur);
+  ids_issue(cur, true, cur.a);
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  ids_offsets(cur);
   int ring = 0;                      // ring buffer of the current tile's stage 0
   // stages 0-2 and the token-row half of stage 3 (the weight half of stage
   // x + 3 is issued in stage x's first step, the token-row half of stage
@@ -365,8 +394,14 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
     ring = __builtin_amdgcn_readfirstlane(ring);
     const int nkb = __builtin_amdgcn_readfirstlane(cur.nkb);
     const int nv = __builtin_amdgcn_readfirstlane(cur.nv);
-    int tn = -1;                     // the next tile (decoded four stages before the end)
-    bool has_next = false;
+    // the next tile, decoded here where the accumulators hold nothing; its
+    // token ids land in LDS behind this tile's first loads (the waits of
+    // stages 0 and 1 count the one load, and stage 2's wait covers it)
+    const int tn = tile_at(round + 1);
+    const bool has_next = tn >= 0;
+    if (has_next) decode(tn, nxt);
+    else nxt = cur;
+    ids_issue(nxt, has_next, cur.a);
 
     // one 16-wide K step over the wave's NV live token blocks; op(k) is the
     // memory operation issued after the k-th MFMA (k = 0..15; the ones past
@@ -401,20 +436,22 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
       const int wk = wnx ? x + 3 - nkb : x + 3;
       const unsigned char* w0 = uni((wnx ? nxt.w[0] : cur.w[0]) + 2048 * wk);
       const unsigned char* w1 = uni((wnx ? nxt.w[1] : cur.w[1]) + 2048 * wk);
+      // the next tile's row offsets, before its first load (step 1 of stage
+      // nkb - 4); its ids landed by stage 2's wait (nkb >= 8)
+      if (x == nkb - kLNS && has_next) ids_offsets(nxt);
       step(f0, nv_tag, [&](int k) __attribute__((always_inline)) {
         if ((k & 1) == 0) read_op(cur.tb0, b0, 1, op_order(k >> 1), f1);
         else if ((k & 3) == 1) issue_b(w0, w1, l3, k >> 2);
       });
-      if (x == nkb - kLNS) {
-        tn = tile_at(round + 1);
-        has_next = tn >= 0;
-        if (has_next) decode(tn, nxt);
-        else nxt = cur;
-      }
       // after stage x + 1's last load came both halves of stages x + 2 and
-      // x + 3 and, for stages 1 and 2, the previous tile's stores
-      if (stored && x <= 1) wait_vm<kStores>(2, true);
-      else wait_vm<kStores>(2, false);
+      // x + 3 and, for stages 0 and 1, the next tile's id load and the
+      // previous tile's stores
+      if (x <= 1) {
+        if (stored) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLLoads + 1 + kStores));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLLoads + 1));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLLoads));
+      }
       // every wave's reads of stage x were issued in its first step: done
       // before the barrier hands the buffer to stage x + 4
       __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
@@ -470,32 +507,37 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
       for (int x = 2; x < tail; ++x) fast(x, pa, pw0, pw1, nv_tag);
       for (int x = tail; x < nkb; ++x) stage(x, nv_tag);
     };
-    switch (nv) {
-      case 4: k_loop(std::integral_constant<int, 4>{}); break;
-      case 3: k_loop(std::integral_constant<int, 3>{}); break;
-      case 2: k_loop(std::integral_constant<int, 2>{}); break;
-      default: k_loop(std::integral_constant<int, 1>{}); break;
-    }
-
     // ---- epilogue: round, pack and store.  Lane l holds token l mod 32 of a
     // block and columns 8q + 4 (l / 32) + 0..3 (q = 0..3) of a 32-column
     // block; one lane-pair swap gives lane l columns 16p + 0..7 and lane l + 32
-    // columns 16p + 8..15.
-    {
+    // columns 16p + 8..15.  A wave with NV < 4 live blocks rewrites its first
+    // block's outputs in the slots of the others (same addresses, same bits),
+    // so every wave issues the same number of stores.
+    auto epilogue = [&](auto nv_tag) __attribute__((always_inline)) {
+      constexpr int NV = decltype(nv_tag)::value;
       const LTile& o = cur;
-      uint4 first[kJ][2];            // the wave's first block, rewritten by skipped blocks
+      uint4 first[NV < 4 ? kJ : 1][2];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int tb = m == 0 ? o.tb0 : 2 * m + wr;
-        const bool live = m == 0 || m < nv;
+        const bool live = m < NV;
         const int row = min(32 * (live ? tb : o.tb0) + (lane & 31), o.valid - 1);
-        bf16_t* rowp = o.out + static_cast<size_t>(row) * o.ld + 8 * (lane >> 5);
+        // 32-bit byte offsets from the tile's (uniform) output base
+        const uint32_t rowoff = (static_cast<uint32_t>(row) * static_cast<uint32_t>(o.ld) +
+                                 8u * static_cast<uint32_t>(lane >> 5)) * 2u;
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             uint4 v;
             if (live) {
+              // read this block's accumulators only now: without the (empty)
+              // asm the compiler copies every accumulator out of the AGPRs at
+              // once and spills to make room
+              if (p == 0) {
+                asm volatile("" : "+a"(acc[m][j]));
+                if constexpr (MODE == kGateUp) asm volatile("" : "+a"(acc[m][j + 2]));
+              }
               uint32_t w[2][2];
 #pragma unroll
               for (int h = 0; h < 2; ++h) {
@@ -520,17 +562,31 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
                 w[1][c] = sw[1];
               }
               v = make_uint4(w[0][0], w[0][1], w[1][0], w[1][1]);
-              if (m == 0) first[j][p] = v;
+              if constexpr (NV < 4) {
+                if (m == 0) first[j][p] = v;
+              }
             } else {
-              v = first[j][p];
+              if constexpr (NV < 4) v = first[j][p];
             }
-            *reinterpret_cast<uint4*>(rowp + 32 * j + 16 * p) = v;
+            // a global store (not flat: a flat store would also count in
+            // lgkmcnt, which the next stages' LDS waits use)
+            typedef __attribute__((address_space(1))) unsigned char gbyte;
+            typedef __attribute__((address_space(1))) u32x4 gu32x4;
+            *(gu32x4*)((gbyte*)o.out + rowoff + (32 * j + 16 * p) * 2) = u32x4{v.x, v.y, v.z, v.w};
             // a few accumulators at a time
             __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
+    };
+
+    switch (nv) {
+      case 4: k_loop(std::integral_constant<int, 4>{}); epilogue(std::integral_constant<int, 4>{}); break;
+      case 3: k_loop(std::integral_constant<int, 3>{}); epilogue(std::integral_constant<int, 3>{}); break;
+      case 2: k_loop(std::integral_constant<int, 2>{}); epilogue(std::integral_constant<int, 2>{}); break;
+      default: k_loop(std::integral_constant<int, 1>{}); epilogue(std::integral_constant<int, 1>{}); break;
     }
+
     stored = true;
     ring = (ring + nkb) & (kLNS - 1);
     ++round;
@@ -547,8 +603,8 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
 bool lds_gemm_fits(int mode, const GemmArgs& a) {
   const int cols = mode == kGateUp ? kLBN / 2 : kLBN;
   if (a.E > kGemmMaxE) return false;
-  if (a.E > 0 && (a.K % kLBK != 0 || a.K < kLNS * kLBK || a.N % cols != 0)) return false;
-  if (a.has_shared && (a.Ks % kLBK != 0 || a.Ks < kLNS * kLBK || a.Ns % cols != 0)) return false;
+  if (a.E > 0 && (a.K % kLBK != 0 || a.K < 8 * kLBK || a.N % cols != 0)) return false;
+  if (a.has_shared && (a.Ks % kLBK != 0 || a.Ks < 8 * kLBK || a.Ns % cols != 0)) return false;
   return true;
 }
 

@@ -37,10 +37,10 @@ of each expert in ascending token order (sorted_token), and slot_of[t, j], the
 position of (t, j) in that order.
 
 Parity pins (tests/test_oracle_pins.py): brute-force per-token dense evaluation
-of every expert with rank-counting selection, the routing invariants, closed
-forms (zero router, k = E, k = 1, zero down projections, x = 0, E = k = 1),
-hand-derived single-channel values, and the parameter counts of the
-"Laguna-M.1-base" card.
+of every expert with rank-counting selection (and of expert_rows' h and y rows),
+the routing invariants, closed forms (zero router, k = E, k = 1, zero down
+projections, x = 0, E = k = 1), hand-derived single-channel values, and the
+parameter counts of the "Laguna-M.1-base" card.
 """
 from __future__ import annotations
 

@@ -343,6 +343,27 @@ def test_shared_expert_on_its_own_stream_matches_the_fused_path(name):
     assert torch.equal(b.y_perm[:n], fused.y_perm[:n])
 
 
+@pytest.mark.parametrize("shape", ["small_ragged", "lds_tiled"])
+def test_grouped_ffn_entry_point_takes_packed_weights(shape):
+    """moe_grouped_ffn, the boundary's single grouped-FFN call, with weights
+    packed by moe_pack_weights (its documented precondition) and token rows
+    gathered through sorted_token (no x_perm): the same bits as the two GEMM
+    calls of the layer pass, whose output the oracle checks."""
+    s = SMALL_BF16 if shape == "small_ragged" else LDS_TILED[0]
+    inp = StackedInputs(LayerInputs(s))
+    x, w, b = run_layer(s, inp, gather=True)
+    c = binding.make_shape(s)
+    h = torch.full_like(b.h, 3.0)
+    y = torch.full_like(b.y_perm, 3.0)
+    ys = torch.full_like(b.y_shared, 3.0)
+    binding.moe_grouped_ffn(c, None, b.sorted_token, x, b.offsets, w.w_gate_up, w.w_down, w.ws_gate_up,
+                            w.ws_down, h, y, ys)
+    torch.cuda.synchronize()
+    assert torch.equal(h.view(torch.int16), b.h.view(torch.int16))
+    assert torch.equal(y.view(torch.int16), b.y_perm.view(torch.int16))
+    assert torch.equal(ys.view(torch.int16), b.y_shared.view(torch.int16))
+
+
 def test_empty_batch_is_a_no_op():
     s = configs.variant(SMALL_BF16, T=0)
     c = binding.make_shape(s)
