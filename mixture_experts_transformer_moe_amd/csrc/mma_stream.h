@@ -105,6 +105,21 @@ __device__ __forceinline__ const unsigned char* stream_wstep(const StreamSrc<BM,
   return s.w[j] + step * 1024;
 }
 
+// One 16-byte weight load.  NT: a non-temporal load, for weights that no
+// other tile of the launch reads again (the line is not kept in L2 / MALL at the
+// expense of the token rows and outputs that are).
+template <bool NT>
+__device__ __forceinline__ u32x4 load_weights(const unsigned char* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Whether a tile shape's weight loads are non-temporal: the tall and short
+// row blocks meant for up to ~200 rows per expert, where an expert's rows
+// mostly sit in one block and its weights stream once per launch.
+template <int BM>
+constexpr bool kStreamWeightsOnce = BM != 96;
+
 // What stays in flight between tiles.
 template <int NB, int PF>
 struct StreamState {
@@ -138,7 +153,7 @@ __device__ __forceinline__ void stream_start(const StreamSrc<BM, NB>& s, StreamS
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) ss.bq[p][j] = *reinterpret_cast<const u32x4*>(stream_wstep(s, j, p) + lane * 16);
+    for (int j = 0; j < NB; ++j) ss.bq[p][j] = load_weights<kStreamWeightsOnce<BM>>(stream_wstep(s, j, p) + lane * 16);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -307,7 +322,7 @@ __device__ __forceinline__ void stream_tile(const StreamSrc<BM, NB>& cur, Stream
         for (int j = 0; j < NB; ++j) {
           const unsigned char* src = from_next ? tail_w[j] + (RSB * u + rs + PF - 4 * RSB) * tail_stride
                                                : stream_wstep(cur, j, RSB * kb + rs + PF);
-          ss.bq[slot][j] = *reinterpret_cast<const u32x4*>(src + lane * 16);
+          ss.bq[slot][j] = load_weights<kStreamWeightsOnce<BM>>(src + lane * 16);
         }
       }
       // keep each refill right after the step that frees its registers: the
