@@ -10,9 +10,9 @@ tokens/s of the layer, plus
 
   roofline      the dominant kernel (the gate/up grouped GEMM with its SwiGLU
                 epilogue): algorithmic bytes (or FLOPs) per launch divided by the
-                median duration of its launches, measured with HIP events recorded
-                on the stream it runs on, in an untimed pass right after the timed
-                steps, against the MI355X peak that bounds it;
+                mean duration of its launches in the timed steps, each bracketed
+                by HIP events recorded on the stream it runs on, against the
+                MI355X peak that bounds it;
   grouped_ffn   the two grouped GEMMs together (gate/up + down), priced the same
                 way: MFMA share of the bf16 peak, and HBM share for the bytes;
   cpu_baseline  the CPU oracle (fp64 NumPy, self-contained routing) timed on the
@@ -51,8 +51,8 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 
 # HBM bytes of one gate/up launch as read by rocprofv3 (FETCH_SIZE and WRITE_SIZE,
-# KiB per dispatch, one counter per run of this script with --copy-mib 1024),
-# each scaled by what the same counter reads for a plain 1 GiB device copy
+# KiB per dispatch, one counter per run of this script with --copy-mib 256),
+# each scaled by what the same counter reads for a plain 256 MiB device copy
 # (FETCH_SIZE reads half of the copy's bytes, WRITE_SIZE all of them).  A record
 # holds only for the kernel sources it was taken on: after any change to them
 # the traffic is reported as null until the counters are taken again.
@@ -62,8 +62,14 @@ GEMM_SOURCES = ("grouped_gemm.hip", "grouped_gemm_lds.hip", "grouped_gemm.h", "m
                 "moe_internal.h")
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
-    "xs2_bf16_t4096_d2048": (662779.1, 37054.2,
-                             "45cf557f44914b82175ec326ecca5e4ebdc36c2c4b79d39d8b25e2746143d312"),
+    "prefill_outlier_bf16_t32768_d2048": (1825064.8, 296003.2,
+                                          "9671c340a66061a05d3556d3847ff5d15bae5852a99fd1d8b2c544502cf9513e"),
+    "xs2_bf16_t4096_d2048": (657259.5, 36882.5,
+                             "9671c340a66061a05d3556d3847ff5d15bae5852a99fd1d8b2c544502cf9513e"),
+    "m1_bf16_t8192_d4096": (3287207.7, 147467.4,
+                            "9671c340a66061a05d3556d3847ff5d15bae5852a99fd1d8b2c544502cf9513e"),
+    "decode_zipf_bf16_t32_d4096": (493888.3, 576.0,
+                                   "9671c340a66061a05d3556d3847ff5d15bae5852a99fd1d8b2c544502cf9513e"),
 }
 
 
