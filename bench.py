@@ -285,6 +285,47 @@ def copy_calibration(mib: int, dev) -> None:
     del src, dst
 
 
+def vendor_gemm(s: configs.MoEShape) -> None:
+    """The vendor library (torch.bmm / torch.mm, bf16) on the layer's expert
+    products with every expert given the mean rows per expert (k T / E): the
+    routed gate/up [E, M, D] x [E, D, 2F], down [E, M, F] x [E, F, D], and the
+    shared expert's two products.  Context only: uniform shapes, no gather, no
+    SwiGLU, no tile table; prints one JSON line."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    M = max(1, s.S // s.E)
+
+    def timed(f, n=20):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:          # clocks settle under load
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    out = {"workload": s.name, "rows_per_expert": M}
+    for name, (bt, m, k, n) in {"gate_up": (s.E, M, s.D, 2 * s.F), "down": (s.E, M, s.F, s.D),
+                                "shared_gate_up": (1, s.T, s.D, 2 * s.Fs),
+                                "shared_down": (1, s.T, s.Fs, s.D)}.items():
+        if n == 0 or k == 0:
+            continue
+        a = torch.randn(bt, m, k, device=dev, dtype=torch.bfloat16, generator=g)
+        w = torch.randn(bt, k, n, device=dev, dtype=torch.bfloat16, generator=g).contiguous()
+        ms = timed(lambda: torch.bmm(a, w)) if bt > 1 else timed(lambda: torch.mm(a[0], w[0]))
+        fl = 2.0 * bt * m * n * k
+        out[name] = {"shape": [bt, m, k, n], "us": round(ms * 1e3, 1),
+                     "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del a, w
+    print(json.dumps(out), flush=True)
+
+
 def train_main(args):
     """One step = the training pass: masked route, permute, load statistics,
     gate/up keeping the pre-activations, down, combine; then the combine
@@ -395,12 +436,19 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB device to device "
                          "three times (a plain copy of known size, to calibrate HBM byte counters)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="instead of the layer: time the vendor library's batched bf16 GEMM (torch.bmm) "
+                         "on the workload's expert products at uniform rows per expert, as context for "
+                         "the grouped GEMMs' MFMA fraction")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's "
               "multi-GPU sharding is a design note, not a measured path.", file=sys.stderr)
         sys.exit(2)
 
+    if args.vendor_gemm:
+        vendor_gemm(configs.get(args.workload))
+        return
     if args.train:
         if args.workload == configs.BENCH_WORKLOAD:
             args.workload = configs.XS2_TRAIN_T4096.name
