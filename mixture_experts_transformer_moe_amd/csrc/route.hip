@@ -118,13 +118,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
 }
 
-// Router logits, bf16: a workgroup of NW waves (4, or 8 for 128 x 64 blocks)
+// Router logits, bf16: a workgroup of NW waves (4, or 8 for the large blocks)
 // computes a TM x TN block of logits (tokens x experts) over the whole of D.
 // Wave w sits at (tm, tn, ks):
-// it owns the MF x MF block (tm, tn) and, when the four waves split K (KS = 4
-// for small batches, so that few tokens still keep 4 load streams per CU),
-// the K blocks ks, ks + KS, ...; the partial blocks are summed in LDS in ks
-// order.  Token rows and router rows reach LDS by direct global->LDS loads
+// it owns WM x WN MF x MF blocks (tokens WM tm .., experts WN tn ..; WM = WN =
+// 2 in the largest block shape, so each fragment read from LDS feeds two
+// MFMAs) and, when the four waves split K (KS = 4 for small batches, so that
+// few tokens still keep 4 load streams per CU), the K blocks ks, ks + KS, ...;
+// the partial blocks are summed in LDS in ks order.  Token rows and router rows reach LDS by direct global->LDS loads
 // (each covers 8 rows x 128 bytes, XOR-swizzled) through a ring of NS stages
 // of KS 64-wide K blocks, the same number of loads per wave in every stage, so
 // every wait is a constant.  MFMA with the router rows as the first operand:
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 // smallest batches: 4 times the workgroups, each reading half the rows;
 // v_mfma_f32_16x16x32_bf16): lane l holds token (l mod 16) and experts
 // 4 (l / 16) + 0..3.
-template <int TM, int TN, int KS, int NS, int NW = 4>
+template <int TM, int TN, int KS, int NS, int NW = 4, int WM = 1, int WN = 1>
 __global__ __launch_bounds__(64 * NW, 1) void route_bf16_kernel(const bf16_t* __restrict__ x,
                                                             const bf16_t* __restrict__ wr,
                                                             const float* __restrict__ bias,
@@ -145,8 +146,10 @@ __global__ __launch_bounds__(64 * NW, 1) void route_bf16_kernel(const bf16_t* __
   constexpr int kStageElems = KS * kBlockElems;
   constexpr int kLoads = KS * kRows / 8;               // 1 KB loads per stage
   constexpr int LPW = kLoads / NW;                     // per wave
-  static_assert((TM / MF) * (TN / MF) * KS == NW && kLoads % NW == 0, "NW waves, equal loads per stage");
+  static_assert((TM / (MF * WM)) * (TN / (MF * WN)) * KS == NW && kLoads % NW == 0,
+                "NW waves, equal loads per stage");
   static_assert(MF == 32 || (TM == 16 && TN == 16), "16 x 16 blocks: one per wave");
+  static_assert(KS == 1 || WM * WN == 1, "split K: one block per wave");
   static_assert(NS * kStageElems * 2 <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) bf16_t lds[NS * kStageElems];
   const int tiles_n = (E + TN - 1) / TN;
@@ -163,8 +166,8 @@ __global__ __launch_bounds__(64 * NW, 1) void route_bf16_kernel(const bf16_t* __
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int ks = wave % KS;
-  const int tm = (wave / KS) % (TM / MF);
-  const int tn = (wave / KS) / (TM / MF);
+  const int tm = (wave / KS) % (TM / (MF * WM));
+  const int tn = (wave / KS) / (TM / (MF * WM));
   const int NKB = D / kPipeBK;                         // a multiple of KS
 
   // this lane's LPW loads per stage: load q of wave w is load i = LPW w + q of
@@ -202,9 +205,16 @@ __global__ __launch_bounds__(64 * NW, 1) void route_bf16_kernel(const bf16_t* __
 
   using Acc = std::conditional_t<MF == 32, f32x16, f32x4>;
   constexpr int NR = MF == 32 ? 16 : 4;                // accumulator registers
-  Acc acc = Acc{0.f};
-  const int arow = MF * tm + (lane & (MF - 1));
-  const int brow = TM + MF * tn + (lane & (MF - 1));
+  Acc acc[WM][WN];
+#pragma unroll
+  for (int m = 0; m < WM; ++m)
+#pragma unroll
+    for (int n = 0; n < WN; ++n) acc[m][n] = Acc{0.f};
+  int arow[WM], brow[WN];
+#pragma unroll
+  for (int m = 0; m < WM; ++m) arow[m] = MF * (WM * tm + m) + (lane & (MF - 1));
+#pragma unroll
+  for (int n = 0; n < WN; ++n) brow[n] = TM + MF * (WN * tn + n) + (lane & (MF - 1));
   int slot = 0;
   for (int s = 0; s < nst; ++s) {
     // this stage was issued NS - 1 stages ago; the NS - 2 later ones (LPW
@@ -217,19 +227,29 @@ __global__ __launch_bounds__(64 * NW, 1) void route_bf16_kernel(const bf16_t* __
     // step.  A step covers 16 (32 x 32 blocks) or 32 (16 x 16) of the 64 K
     // values; lane l takes 16-byte chunk l / MF of the step's chunks.
     constexpr int kSteps = MF == 32 ? 4 : 2;
-    bf16x8 fa[kSteps], fb[kSteps];
+    bf16x8 fa[WM][kSteps], fb[WN][kSteps];
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
       const int ch = (8 / kSteps) * i + lane / MF;
-      fb[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&blk[pipe_swz(brow, ch)]));
-      fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&blk[pipe_swz(arow, ch)]));
+#pragma unroll
+      for (int n = 0; n < WN; ++n)
+        fb[n][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&blk[pipe_swz(brow[n], ch)]));
+#pragma unroll
+      for (int m = 0; m < WM; ++m)
+        fa[m][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&blk[pipe_swz(arow[m], ch)]));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
-      if constexpr (MF == 32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[i], acc, 0, 0, 0);
-      else acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[i], fa[i], acc, 0, 0, 0);
-    }
+    for (int i = 0; i < kSteps; ++i)
+#pragma unroll
+      for (int m = 0; m < WM; ++m)
+#pragma unroll
+        for (int n = 0; n < WN; ++n) {
+          if constexpr (MF == 32)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[n][i], fa[m][i], acc[m][n], 0, 0, 0);
+          else
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[n][i], fa[m][i], acc[m][n], 0, 0, 0);
+        }
     slot = slot + 1 == NS ? 0 : slot + 1;
   }
   // the tail loads (clamped repeats) land before LDS is reused or the
@@ -239,7 +259,7 @@ __global__ __launch_bounds__(64 * NW, 1) void route_bf16_kernel(const bf16_t* __
     __builtin_amdgcn_s_barrier();
     float* red = reinterpret_cast<float*>(lds);        // [KS][NR][64]
 #pragma unroll
-    for (int r = 0; r < NR; ++r) red[(ks * NR + r) * 64 + lane] = acc[r];
+    for (int r = 0; r < NR; ++r) red[(ks * NR + r) * 64 + lane] = acc[0][0][r];
     __syncthreads();
     if (ks != 0) return;
 #pragma unroll
@@ -247,25 +267,31 @@ __global__ __launch_bounds__(64 * NW, 1) void route_bf16_kernel(const bf16_t* __
       float v = red[r * 64 + lane];
 #pragma unroll
       for (int j = 1; j < KS; ++j) v += red[(j * NR + r) * 64 + lane];
-      acc[r] = v;
+      acc[0][0][r] = v;
     }
   }
-  const int t = t0 + MF * tm + (lane & (MF - 1));
-  if (t >= T) return;
 #pragma unroll
-  for (int q = 0; q < NR / 4; ++q) {
-    // 4 adjacent experts
-    const int e = e0 + MF * tn + (MF == 32 ? mfma32_row(4 * q, lane) : 4 * (lane >> 4));
-    float z[4];
+  for (int m = 0; m < WM; ++m) {
+    const int t = t0 + MF * (WM * tm + m) + (lane & (MF - 1));
+    if (t >= T) continue;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) z[c] = acc[4 * q + c] + ((bias && e + c < E) ? bias[min(e + c, E - 1)] : 0.f);
-    float* dst = logits + static_cast<size_t>(t) * E + e;
-    if ((E & 3) == 0 && e + 4 <= E) {
-      *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
-    } else {
-      for (int c = 0; c < 4; ++c)
-        if (e + c < E) dst[c] = z[c];
-    }
+    for (int n = 0; n < WN; ++n)
+#pragma unroll
+      for (int q = 0; q < NR / 4; ++q) {
+        // 4 adjacent experts
+        const int e = e0 + MF * (WN * tn + n) + (MF == 32 ? mfma32_row(4 * q, lane) : 4 * (lane >> 4));
+        float z[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          z[c] = acc[m][n][4 * q + c] + ((bias && e + c < E) ? bias[min(e + c, E - 1)] : 0.f);
+        float* dst = logits + static_cast<size_t>(t) * E + e;
+        if ((E & 3) == 0 && e + 4 <= E) {
+          *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
+        } else {
+          for (int c = 0; c < 4; ++c)
+            if (e + c < E) dst[c] = z[c];
+        }
+      }
   }
 }
 
@@ -307,7 +333,13 @@ hipError_t launch_route_bf16(const moe_shape& s, const bf16_t* x, const bf16_t* 
   const int huge = ((s.T + 127) / 128) * ((s.E + 63) / 64);
   const int big = ((s.T + 63) / 64) * ((s.E + 63) / 64);
   const int mid = ((s.T + 31) / 32) * ((s.E + 31) / 32);
-  if (huge >= 256) {
+  if (s.E == 256 && (s.T + 127) / 128 >= 256) {
+    // all 256 experts of 128 tokens per workgroup, each wave 64 x 64 (every
+    // fragment read from LDS feeds two MFMAs): half the bytes into LDS per
+    // logit of the 128 x 64 blocks, and still a block per CU
+    route_bf16_kernel<128, 256, 1, 3, 8, 2, 2><<<(s.T + 127) / 128, 512, 0, st>>>(x, wr, bias, logits, s.T,
+                                                                                s.D, s.E);
+  } else if (huge >= 256) {
     // 128 x 64 blocks, 8 waves: a quarter fewer bytes into LDS per logit
     route_bf16_kernel<128, 64, 1, 4, 8><<<huge, 512, 0, st>>>(x, wr, bias, logits, s.T, s.D, s.E);
   } else if (big >= 128) {
