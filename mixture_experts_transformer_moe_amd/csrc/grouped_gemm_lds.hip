@@ -510,74 +510,105 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
     // ---- epilogue: round, pack and store.  Lane l holds token l mod 32 of a
     // block and columns 8q + 4 (l / 32) + 0..3 (q = 0..3) of a 32-column
     // block; one lane-pair swap gives lane l columns 16p + 0..7 and lane l + 32
-    // columns 16p + 8..15.  A wave with NV < 4 live blocks rewrites its first
-    // block's outputs in the slots of the others (same addresses, same bits),
-    // so every wave issues the same number of stores.
+    // columns 16p + 8..15.  Stored that way, a 16-byte-per-lane store writes 32
+    // bytes into each of 32 rows, and the L2 takes 32 partial-line writes per
+    // store (measured: the down kernel's stores cost it a quarter of its time
+    // on the long prefill).  So each 32-row x 64-column piece (4 KB) goes
+    // through LDS: the lanes write their chunks row-major (16-byte chunks
+    // XOR-swizzled by row / 2, conflict-free both ways), read back 8 rows x 128
+    // bytes per store, and each store writes 8 whole 128-byte row segments.
+    // The staging area is this wave's 4 KB of the weight half of the tile's
+    // last ring buffer: every wave has read that stage before the barrier of
+    // the tile's last stage, and the next load into it is this wave's own (the
+    // next tile's stage 0 issues it, after the wait at the end of here).  A
+    // wave with NV < 4 live blocks rewrites its first block's outputs in the
+    // slots of the others (same addresses, same bits), so every wave issues the
+    // same number of stores.
     auto epilogue = [&](auto nv_tag) __attribute__((always_inline)) {
       constexpr int NV = decltype(nv_tag)::value;
+      constexpr int kHalves = kJ / 2;                // 64-column pieces of the wave's columns
       const LTile& o = cur;
-      uint4 first[NV < 4 ? kJ : 1][2];
+      unsigned char* stg = smem + ((ring + nkb - 1) & (kLNS - 1)) * kLStage + kLStageA + wave * 4096;
+      u32x4 first[NV < 4 ? kHalves : 1][4];
+      typedef __attribute__((address_space(1))) unsigned char gbyte;
+      typedef __attribute__((address_space(1))) u32x4 gu32x4;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int tb = m == 0 ? o.tb0 : 2 * m + wr;
         const bool live = m < NV;
-        const int row = min(32 * (live ? tb : o.tb0) + (lane & 31), o.valid - 1);
-        // 32-bit byte offsets from the tile's (uniform) output base
-        const uint32_t rowoff = (static_cast<uint32_t>(row) * static_cast<uint32_t>(o.ld) +
-                                 8u * static_cast<uint32_t>(lane >> 5)) * 2u;
 #pragma unroll
-        for (int j = 0; j < kJ; ++j) {
+        for (int hc = 0; hc < kHalves; ++hc) {
+          u32x4 out4[4];
+          if (live) {
 #pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            uint4 v;
-            if (live) {
+            for (int jj = 0; jj < 2; ++jj) {
+              const int j = 2 * hc + jj;
               // read this block's accumulators only now: without the (empty)
               // asm the compiler copies every accumulator out of the AGPRs at
               // once and spills to make room
-              if (p == 0) {
-                asm volatile("" : "+a"(acc[m][j]));
-                if constexpr (MODE == kGateUp) asm volatile("" : "+a"(acc[m][j + 2]));
-              }
-              uint32_t w[2][2];
+              asm volatile("" : "+a"(acc[m][j]));
+              if constexpr (MODE == kGateUp) asm volatile("" : "+a"(acc[m][j + 2]));
 #pragma unroll
-              for (int h = 0; h < 2; ++h) {
-                const int q = 2 * p + h;
-                float y[4];
+              for (int p = 0; p < 2; ++p) {
+                uint32_t w[2][2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  if constexpr (MODE == kGateUp) {
-                    const float gv = acc[m][j][4 * q + e], uv = acc[m][j + 2][4 * q + e];
-                    y[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-                  } else {
-                    y[e] = acc[m][j][4 * q + e];
+                for (int h = 0; h < 2; ++h) {
+                  const int q = 2 * p + h;
+                  float y[4];
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) {
+                    if constexpr (MODE == kGateUp) {
+                      const float gv = acc[m][j][4 * q + e], uv = acc[m][j + 2][4 * q + e];
+                      y[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+                    } else {
+                      y[e] = acc[m][j][4 * q + e];
+                    }
                   }
+                  w[h][0] = pack_bf16x2(y[0], y[1]);
+                  w[h][1] = pack_bf16x2(y[2], y[3]);
                 }
-                w[h][0] = pack_bf16x2(y[0], y[1]);
-                w[h][1] = pack_bf16x2(y[2], y[3]);
-              }
 #pragma unroll
-              for (int c = 0; c < 2; ++c) {
-                const auto sw = __builtin_amdgcn_permlane32_swap(w[0][c], w[1][c], false, false);
-                w[0][c] = sw[0];
-                w[1][c] = sw[1];
+                for (int c = 0; c < 2; ++c) {
+                  const auto sw = __builtin_amdgcn_permlane32_swap(w[0][c], w[1][c], false, false);
+                  w[0][c] = sw[0];
+                  w[1][c] = sw[1];
+                }
+                // chunk c of row r (columns 8c .. 8c + 7 of the piece)
+                const int r = lane & 31, c = 4 * jj + 2 * p + (lane >> 5);
+                *reinterpret_cast<u32x4*>(stg + r * 128 + ((c ^ ((r >> 1) & 7)) << 4)) =
+                    u32x4{w[0][0], w[0][1], w[1][0], w[1][1]};
               }
-              v = make_uint4(w[0][0], w[0][1], w[1][0], w[1][1]);
-              if constexpr (NV < 4) {
-                if (m == 0) first[j][p] = v;
-              }
-            } else {
-              if constexpr (NV < 4) v = first[j][p];
             }
-            // a global store (not flat: a flat store would also count in
-            // lgkmcnt, which the next stages' LDS waits use)
-            typedef __attribute__((address_space(1))) unsigned char gbyte;
-            typedef __attribute__((address_space(1))) u32x4 gu32x4;
-            *(gu32x4*)((gbyte*)o.out + rowoff + (32 * j + 16 * p) * 2) = u32x4{v.x, v.y, v.z, v.w};
-            // a few accumulators at a time
-            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int sidx = 0; sidx < 4; ++sidx) {
+              const int r = 8 * sidx + (lane >> 3), c = lane & 7;
+              out4[sidx] = *reinterpret_cast<const u32x4*>(stg + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+              if constexpr (NV < 4) {
+                if (m == 0) first[hc][sidx] = out4[sidx];
+              }
+            }
+          } else {
+#pragma unroll
+            for (int sidx = 0; sidx < 4; ++sidx) {
+              if constexpr (NV < 4) out4[sidx] = first[hc][sidx];
+            }
           }
+          // store sidx: rows 8 sidx + lane / 8 of the block, columns 64 hc +
+          // 8 (lane mod 8) .. + 7; a global store (not flat: a flat store
+          // would also count in lgkmcnt, which the next stages' LDS waits use)
+#pragma unroll
+          for (int sidx = 0; sidx < 4; ++sidx) {
+            const int row = min(32 * (live ? tb : o.tb0) + 8 * sidx + (lane >> 3), o.valid - 1);
+            const uint32_t off = (static_cast<uint32_t>(row) * static_cast<uint32_t>(o.ld) +
+                                  static_cast<uint32_t>(64 * hc + 8 * (lane & 7))) * 2u;
+            *(gu32x4*)((gbyte*)o.out + off) = out4[sidx];
+          }
+          // a few accumulators at a time
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // the staging reads are done before this wave's next load into the area
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
     };
 
     switch (nv) {
