@@ -64,7 +64,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   constexpr int kWaveCols = (MODE == kGateUp) ? 16 * NB : 32 * NB;
   constexpr int kOutCols = 4 * kWaveCols;
   __shared__ __attribute__((aligned(16))) bf16_t lds[kStreamNS * ST::kAElems];
-  static_assert(kStreamNS * ST::kAElems * 2 + 2 * (kMaxE + 1) * 4 <= 160 * 1024, "LDS");
+  // output staging: per wave one token block of its row segments (32 rows x
+  // kRowB bytes), see store_block below
+  constexpr int kRowB = kWaveCols * 2;
+  __shared__ __attribute__((aligned(16))) unsigned char stg_all[4][32 * kRowB];
+  static_assert(kStreamNS * ST::kAElems * 2 + 4 * 32 * kRowB + 2 * (kMaxE + 1) * 4 <= 160 * 1024, "LDS");
   __shared__ int tile_end[kMaxE + 1];
   __shared__ int row_base[kMaxE + 1];
   __shared__ int shared_bm;
@@ -276,18 +280,50 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   // store at the tile's end (the next tile's first waits count those stores).
   // Rows past the tile's last rewrite its last row, whose values they repeat
   // bit for bit, so the number of stores is a constant.
+  //
+  // A packed value (lane l: token l mod 32 of block m, 8 columns at 32 j +
+  // 16 p + 8 (l / 32)) stored as it is writes 32 bytes into each of 32 rows: 32
+  // partial-line writes for the L2 per store, which measured as a large share
+  // of these kernels' time at the XS.2 shape.  So a block's values go through
+  // this wave's staging area in LDS: written row-major (16-byte chunks
+  // XOR-swizzled, conflict-free for the column-wise writes and the row-wise
+  // reads), read back as whole row segments (kRowB bytes per row: 64, 128 or
+  // 256), 1 KB per store, as many stores as before.
   constexpr int kJ = MODE == kGateUp ? NB / 2 : NB;   // output blocks of 32 columns per wave
   constexpr int kStores = MBW * kJ * 2;
   constexpr bool kDefer = NB == 2;
-  constexpr int kPer = (kStores + 3) / 4;             // stores per tail block
+  constexpr int kChunks = kRowB / 16;                 // 16-byte chunks per row segment (4 kJ)
+  constexpr int kSwzShift = kRowB == 64 ? 2 : (kRowB == 128 ? 1 : 0);
+  static_assert(kChunks == 4 * kJ && (kRowB == 64 || kRowB == 128 || kRowB == 256), "row segments");
+  typedef __attribute__((address_space(1))) unsigned char gbyte;
+  typedef __attribute__((address_space(1))) u32x4 gu32x4;
+  unsigned char* stg = stg_all[__builtin_amdgcn_readfirstlane(tid >> 6)];
+  auto chunk_at = [&](int r, int c) { return stg + r * kRowB + ((c ^ ((r >> kSwzShift) & (kChunks - 1))) << 4); };
   uint4 pend[kStores];
   TileOut opend;
   bool has_pend = false;
-  auto store_pend = [&](int s_idx) {
-    const int m = s_idx / (2 * kJ), j = (s_idx / 2) % kJ, p = s_idx % 2;
-    const int row = min(32 * m + (lane & 31), opend.valid - 1);
-    bf16_t* dst = opend.out + static_cast<size_t>(row) * opend.ld + 8 * (lane >> 5) + 32 * j + 16 * p;
-    *reinterpret_cast<uint4*>(dst) = pend[s_idx];
+  // value (j, p) of block m into the staging area
+  auto stage_value = [&](int j, int p, const uint4& v) {
+    *reinterpret_cast<u32x4*>(chunk_at(lane & 31, 4 * j + 2 * p + (lane >> 5))) = u32x4{v.x, v.y, v.z, v.w};
+  };
+  // the staged block m of tile `o`, read back and stored: store s writes rows
+  // s (64 / kChunks) + l / kChunks, chunk l mod kChunks
+  auto store_staged = [&](int m, const TileOut& o) {
+#pragma unroll
+    for (int s_idx = 0; s_idx < 2 * kJ; ++s_idx) {
+      const int r = s_idx * (64 / kChunks) + lane / kChunks, c = lane % kChunks;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(chunk_at(r, c));
+      const int row = min(32 * m + r, o.valid - 1);
+      const uint32_t off = (static_cast<uint32_t>(row) * static_cast<uint32_t>(o.ld) + 8u * c) * 2u;
+      *(gu32x4*)((gbyte*)o.out + off) = v;
+    }
+  };
+  auto store_block = [&](int m) {
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) stage_value(j, p, pend[(m * kJ + j) * 2 + p]);
+    store_staged(m, opend);
   };
   decode(pos, cur, ocur);
   stream_start<BM, NB, PF>(cur, ss, lds);
@@ -320,8 +356,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
           }
       }
       if (kDefer && has_pend) {
+        // the previous tile's blocks, spread over the 4 tail blocks
 #pragma unroll
-        for (int s_idx = u * kPer; s_idx < (u + 1) * kPer && s_idx < kStores; ++s_idx) store_pend(s_idx);
+        for (int m = MBW * u / 4; m < MBW * (u + 1) / 4; ++m) store_block(m);
       }
     }, ss, lds, acc, !kDefer && has_pend);
     // epilogue: round and pack.  Lane l holds columns 8q + 4 (l / 32) + 0..3
@@ -363,16 +400,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
             v[0][c] = sw[0];
             v[1][c] = sw[1];
           }
-          pend[(m * kJ + j) * 2 + p] = make_uint4(v[0][0], v[0][1], v[1][0], v[1][1]);
-          if (!kDefer) {
-            opend = o;
-            store_pend((m * kJ + j) * 2 + p);
+          const uint4 val = make_uint4(v[0][0], v[0][1], v[1][0], v[1][1]);
+          if constexpr (kDefer) {
+            pend[(m * kJ + j) * 2 + p] = val;
+          } else {
+            stage_value(j, p, val);
             // a few accumulators at a time: reading them all out at once
             // would need as many VGPRs, on top of the weight ring in flight
             __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
+      if constexpr (!kDefer) store_staged(m, o);
     }
     opend = o;
     has_pend = true;
@@ -382,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   // the last tile's outputs
   if (kDefer) {
 #pragma unroll
-    for (int s_idx = 0; s_idx < kStores; ++s_idx) store_pend(s_idx);
+    for (int m = 0; m < MBW; ++m) store_block(m);
   }
   stream_finish();
 }
