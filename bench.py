@@ -62,14 +62,14 @@ GEMM_SOURCES = ("grouped_gemm.hip", "grouped_gemm_lds.hip", "grouped_gemm.h", "m
                 "moe_internal.h")
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
-    "prefill_outlier_bf16_t32768_d2048": (1775644.7, 295864.7,
-                                          "9671c340a66061a05d3556d3847ff5d15bae5852a99fd1d8b2c544502cf9513e"),
-    "xs2_bf16_t4096_d2048": (657259.5, 36882.5,
-                             "9671c340a66061a05d3556d3847ff5d15bae5852a99fd1d8b2c544502cf9513e"),
-    "m1_bf16_t8192_d4096": (3287207.7, 147467.4,
-                            "9671c340a66061a05d3556d3847ff5d15bae5852a99fd1d8b2c544502cf9513e"),
-    "decode_zipf_bf16_t32_d4096": (493888.3, 576.0,
-                                   "9671c340a66061a05d3556d3847ff5d15bae5852a99fd1d8b2c544502cf9513e"),
+    "prefill_outlier_bf16_t32768_d2048": (1909411.2, 295873.7,
+                                          "5e5d44ad59ca826748bf57fe66fa11d18743694cdab9537377cb5e6b8dc46061"),
+    "xs2_bf16_t4096_d2048": (656867.2, 36864.2,
+                             "5e5d44ad59ca826748bf57fe66fa11d18743694cdab9537377cb5e6b8dc46061"),
+    "m1_bf16_t8192_d4096": (3256389.4, 147458.4,
+                            "5e5d44ad59ca826748bf57fe66fa11d18743694cdab9537377cb5e6b8dc46061"),
+    "decode_zipf_bf16_t32_d4096": (493913.0, 576.0,
+                                   "5e5d44ad59ca826748bf57fe66fa11d18743694cdab9537377cb5e6b8dc46061"),
 }
 
 
