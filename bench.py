@@ -18,6 +18,11 @@ tokens/s of the layer, plus
   cpu_baseline  the CPU oracle (fp64 NumPy, self-contained routing) timed on the
                 host cores on the same workload.
 
+Run with no --workload (the driver's invocation), the line also carries
+`train`: the layer's training pass (below) on the padded XS.2 batch, 40 steps
+measured after the forward line's timed region, with its weight-gradient
+roofline.
+
 Before the W warmup steps an untimed settle phase runs steps until at least
 40 of them and 100 ms of device time have passed (the clocks take some tens of
 milliseconds of load to settle); its length is reported as `settle`.
@@ -327,6 +332,11 @@ def vendor_gemm(s: configs.MoEShape) -> None:
 
 
 def train_main(args):
+    """Prints the training pass's JSON line (see train_measure)."""
+    print(json.dumps(train_measure(args)), flush=True)
+
+
+def train_measure(args) -> dict:
     """One step = the training pass: masked route, permute, load statistics,
     gate/up keeping the pre-activations, down, combine; then the combine
     backward, dh and SwiGLU backward, dx, weight and bias gradients."""
@@ -410,7 +420,7 @@ def train_main(args):
         "aux_loss": float(b.aux_loss.item()),
         "roofline": roof, "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+    return line
 
 
 def main():
@@ -419,7 +429,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     # (an untimed settle phase runs before these: at least 40 steps and 100 ms)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=configs.BENCH_WORKLOAD, choices=sorted(configs.WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(configs.WORKLOADS),
+                    help=f"default {configs.BENCH_WORKLOAD} (with the training summary)")
     ap.add_argument("--split-shared", action="store_true",
                     help="run the shared expert on a second stream beside the router and the "
                          "permutation (moe_shared_ffn), the grouped GEMMs over the routed experts only")
@@ -436,11 +447,17 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB device to device "
                          "three times (a plain copy of known size, to calibrate HBM byte counters)")
+    ap.add_argument("--no-train-summary", action="store_true",
+                    help="skip the short training-pass measurement whose summary the default forward "
+                         "line carries (it is taken only when --workload is not given)")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="instead of the layer: time the vendor library's batched bf16 GEMM (torch.bmm) "
                          "on the workload's expert products at uniform rows per expert, as context for "
                          "the grouped GEMMs' MFMA fraction")
     args = ap.parse_args()
+    train_summary = args.workload is None and not args.no_train_summary and not args.train
+    if args.workload is None:
+        args.workload = configs.BENCH_WORKLOAD
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's "
               "multi-GPU sharding is a design note, not a measured path.", file=sys.stderr)
@@ -618,6 +635,18 @@ def main():
         "tokens_per_s_from_call_medians": round(s.T / (sum(calls_ms.values()) * 1e-3), 1),
         "roofline": roof, "grouped_ffn": ffn, "cpu_baseline": cpu,
     }
+    if train_summary:
+        # the layer's training pass on its own workload (the padded XS.2
+        # batch), measured after the forward line's timed region, with no CPU
+        # leg; its full line comes from --train
+        targs = argparse.Namespace(workload=configs.XS2_TRAIN_T4096.name, steps=40, warmup=5,
+                                   no_cpu_baseline=True, x_perm=False, copy_mib=0)
+        t = train_measure(targs)
+        line["train"] = {"workload": t["config"]["workload"], "tokens_per_s": t["value"],
+                         "ms_per_step": t["ms_per_step"], "steps": t["steps"], "settle": t["settle"],
+                         "train_tflops": t["train_tflops"],
+                         "wgrad_roofline": {k: t["roofline"][k] for k in ("bound", "achieved", "peak", "unit",
+                                                                          "frac", "kernel_ms")}}
     print(json.dumps(line), flush=True)
 
 
