@@ -28,7 +28,8 @@
 //     gate block with the up block of the same columns, so SwiGLU is applied in
 //     registers before one rounding to bf16;
 //   * a tile's outputs are stored while the next tile's loads stream (see the
-//     epilogue), 16 bytes per lane after a lane-pair swap.
+//     epilogue), a token block at a time through a small LDS staging area so
+//     that each 16-byte-per-lane store writes whole row segments.
 #include "grouped_gemm.h"
 #include "mma_stream.h"
 
@@ -52,8 +53,8 @@ struct TileOut {
 // rows (gate_up: 128 gate rows and the 128 up rows of the same columns; down:
 // 256 output columns), computed by the weight-streaming pipeline
 // (mma_stream.h).  Wave w holds the gate block and the up block of the same 32
-// columns, so SwiGLU is applied in registers; outputs go straight from
-// registers to memory, eight adjacent bf16 values (16 bytes) per lane and store.
+// columns, so SwiGLU is applied in registers; outputs are rounded in registers
+// and leave through a per-wave LDS staging area as whole row segments.
 template <int MODE, int BM, int NB, int PF, bool W8>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   using ST = StreamTile<BM, NB, PF, W8>;
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   StreamState<NB, PF> ss;
   // A tile's outputs are rounded and packed, 8 bf16 per lane and store.  With
   // 2 weight blocks per wave they wait in registers and are stored during the
-  // next tile's last K blocks, a few per block among its loads: stored at the
+  // next tile's last K blocks, a token block at a time among its loads: stored at the
   // tile's end they would queue behind the next tile's whole prefetch and
   // hold every wave up.  The 4-block shapes have no registers to spare and
   // store at the tile's end (the next tile's first waits count those stores).
