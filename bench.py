@@ -68,13 +68,13 @@ GEMM_SOURCES = ("grouped_gemm.hip", "grouped_gemm_lds.hip", "grouped_gemm.h", "m
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
     "prefill_outlier_bf16_t32768_d2048": (1909411.2, 295873.7,
-                                          "7409c4400c5267fabb00e1a8ec8f23cb08ca8e272be324c0ef2ae71a6b7ca744"),
+                                          "dba5674429f905e79f0f6d19a472947b65ed6f172fe252ed82d1e91f37837114"),
     "xs2_bf16_t4096_d2048": (656867.2, 36864.2,
-                             "7409c4400c5267fabb00e1a8ec8f23cb08ca8e272be324c0ef2ae71a6b7ca744"),
+                             "dba5674429f905e79f0f6d19a472947b65ed6f172fe252ed82d1e91f37837114"),
     "m1_bf16_t8192_d4096": (3256389.4, 147458.4,
-                            "7409c4400c5267fabb00e1a8ec8f23cb08ca8e272be324c0ef2ae71a6b7ca744"),
+                            "dba5674429f905e79f0f6d19a472947b65ed6f172fe252ed82d1e91f37837114"),
     "decode_zipf_bf16_t32_d4096": (493913.0, 576.0,
-                                   "7409c4400c5267fabb00e1a8ec8f23cb08ca8e272be324c0ef2ae71a6b7ca744"),
+                                   "dba5674429f905e79f0f6d19a472947b65ed6f172fe252ed82d1e91f37837114"),
 }
 
 

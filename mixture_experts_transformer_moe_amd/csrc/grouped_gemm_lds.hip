@@ -44,7 +44,10 @@
 //     last rewrite its last row, skipped blocks rewrite the wave's first block,
 //     with the same bits), so the next tile's first waits can count them;
 //   * gate_up pairs each wave's two gate blocks with the up blocks of the same
-//     columns, so SwiGLU is applied in registers before one rounding to bf16.
+//     columns, so SwiGLU is applied in registers before one rounding to bf16;
+//   * outputs leave through LDS (the wave's 4 KB of the tile's last weight
+//     buffer), so that every store writes whole 128-byte row segments; down's
+//     stores are non-temporal (the combine reads them once, later).
 #include "grouped_gemm.h"
 #include <utility>
 
