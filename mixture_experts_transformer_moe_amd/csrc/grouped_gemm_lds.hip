@@ -29,16 +29,22 @@
 //     wave row b mod 2, so a ragged last row block of an expert splits its
 //     blocks evenly over both wave rows, and a wave skips the MFMAs of blocks
 //     that hold no row;
-//   * K advances in stages of 32 through a ring of 4 LDS stages of 32 KB (token
-//     rows, then weight blocks), filled by direct global->LDS loads
-//     (global_load_lds_dwordx4): token rows gathered through `sorted_token`
-//     land as 16 rows x 64 bytes per wave load, XOR-swizzled for conflict-free
-//     ds_read_b128; packed weights land as 1 KB MFMA operand blocks;
+//   * K advances in stages of 32, filled by direct global->LDS loads
+//     (global_load_lds_dwordx4): the weights of a stage (packed 1 KB MFMA
+//     operand blocks, 16 KB) go through a ring of 4 buffers; the token rows go
+//     in pairs of stages, 64 K values = one whole 128-byte line per row (a
+//     wave load: 8 rows), through 2 buffers of 32 KB, XOR-swizzled for
+//     conflict-free ds_read_b128.  Rows gathered through `sorted_token` are
+//     scattered over the activations, and a 1 KB wave load of whole lines
+//     touches 8 lines where one of 64-byte rows (one stage) touches 16
+//     (measured: gate/up 2%, down 4% faster on the long prefill);
 //   * one barrier per stage, between its two MFMA steps: by then every wave has
-//     read the stage before it (whose buffer then takes the stage three ahead)
-//     and each wave has waited for its own loads of the next stage; MFMA
-//     operands are read from LDS one step ahead into a second register set;
-//   * the ring does not drain between tiles: the last stages of a tile load the
+//     read the stage before it (whose weight buffer then takes the stage three
+//     ahead; in an odd stage, the pair buffer of the stage and the one before
+//     it takes the pair three and four ahead) and each wave has waited for its
+//     own loads of the next stage; MFMA operands are read from LDS one step
+//     ahead into a second register set;
+//   * the rings do not drain between tiles: the last stages of a tile load the
 //     next tile's first three stages, and the tile's outputs are stored after
 //     them (a constant number of 16-byte stores per wave: rows past a tile's
 //     last rewrite its last row, skipped blocks rewrite the wave's first block,
@@ -61,30 +67,15 @@ constexpr int kLBM = 256;                 // token rows per tile
 constexpr int kLBN = 256;                 // weight rows per tile
 constexpr int kLBK = 32;                  // K per LDS stage (two 16-wide MFMA steps)
 constexpr int kLNS = 4;                   // LDS stages
-constexpr int kLStageA = kLBM * kLBK * 2; // 16 KB of token rows
-constexpr int kLStage = kLStageA + kLBN * kLBK * 2;   // + 16 KB of weight blocks
-constexpr int kLLoads = 8;                // direct loads per wave and stage
+constexpr int kLPairA = kLBM * 2 * kLBK * 2;   // 32 KB: token rows of two K stages (128 bytes a row)
+constexpr int kLStageB = kLBN * kLBK * 2;      // 16 KB of weight blocks per stage
+constexpr int kLBOff = 2 * kLPairA;            // the weight ring follows the two token-row pair buffers
 
-// Chunk swizzle of a 64-byte token row in LDS: 16-byte chunk c of tile row r
-// sits at slot c ^ lswz(r).  A ds_read_b128 of 32 rows, one chunk each, then
-// hits distinct slots in every group of 16 consecutive rows (4 rows of a
-// 256-byte bank window) and of 8 consecutive rows (2 rows of 128 bytes).
-__device__ __forceinline__ int lswz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
-// s_waitcnt vmcnt(kLLoads * later + (stores ? ST : 0)), later in {0, 1, 2}:
-// the waits below are compile-time constants chosen at run time.
-template <int ST>
-__device__ __forceinline__ void wait_vm(int later, bool stores) {
-  if (stores) {
-    if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLLoads + ST));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(kLLoads + ST));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_only(ST));
-  } else {
-    if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLLoads));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(kLLoads));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-  }
-}
+// Chunk swizzle of a 128-byte token row (a pair of stages) in LDS: 16-byte
+// chunk c of tile row r sits at slot c ^ lswz8(r).  A ds_read_b128 of 32 rows,
+// one chunk each, then hits distinct slots in every group of 16 consecutive
+// rows (8 pairs of rows, each pair one 256-byte bank window).
+__device__ __forceinline__ int lswz8(int r) { return (r >> 1) & 7; }
 
 // s_waitcnt immediate that waits for lgkmcnt <= n only (gfx9 encoding).
 constexpr int lgkmcnt_only(int n) { return 15 | (7 << 4) | ((n & 15) << 8) | (3 << 14); }
@@ -109,7 +100,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Sources of one tile (everything uniform except a_off).
 struct LTile {
   const unsigned char* a;      // token rows: the chunk of load i of K stage kb is at a + 64 kb + a_off[i]
-  uint32_t a_off[4];
+  uint32_t a_off[8];
   const unsigned char* w[2];   // the wave's two weight blocks: K stage kb, step s at w[j] + 2048 kb + 1024 s
   int nkb;                     // K / 32
   int nv;                      // token blocks of this wave that hold rows (1..4)
@@ -146,11 +137,11 @@ __device__ __forceinline__ void dma_lds(const unsigned char* base, uint32_t voff
 
 template <int MODE>
 __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kLNS * kLStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kLBOff + kLNS * kLStageB];
   __shared__ int tile_end[kGemmMaxE + 1];
   __shared__ int row_base[kGemmMaxE + 1];
   __shared__ __attribute__((aligned(256))) int32_t ids_lds[4][64];   // next tile's token ids, per wave
-  static_assert(kLNS * kLStage + 2 * (kGemmMaxE + 1) * 4 + 4 * 64 * 4 <= 160 * 1024, "LDS");
+  static_assert(kLBOff + kLNS * kLStageB + 2 * (kGemmMaxE + 1) * 4 + 4 * 64 * 4 <= 160 * 1024, "LDS");
   constexpr int kOutCols = MODE == kGateUp ? kLBN / 2 : kLBN;    // output columns per tile
   constexpr int kJ = MODE == kGateUp ? 2 : 4;                    // output blocks of 32 per wave
   constexpr int kStores = 4 * kJ * 2;                            // 16-byte stores per wave and tile
@@ -237,9 +228,9 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
     t.nkb = K / kLBK;
     t.valid = valid;
 
-    // token rows: load i of this wave fills tile rows 64 wave + 16 i + 0..15,
-    // lane l row 64 wave + 16 i + l / 4, LDS slot l % 4 = logical chunk
-    // (l % 4) ^ lswz(row); rows past the tile's last repeat it
+    // token rows: load i of this wave fills tile rows 64 wave + 8 i + 0..7,
+    // lane l row 64 wave + 8 i + l / 8, LDS slot l % 8 = logical chunk
+    // (l % 8) ^ lswz8(row); rows past the tile's last repeat it
     const bool gathered = !shared && g.gather != nullptr;
     t.gathered = gathered;
     t.K = K;
@@ -251,9 +242,9 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
       t.a = uni(reinterpret_cast<const unsigned char*>(shared ? g.a_shared + static_cast<size_t>(m0) * K
                                                               : g.a_routed + static_cast<size_t>(rb + m0) * K));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 64 * wave + 16 * i + (ln >> 2);
-        const int c = (ln & 3) ^ lswz(row);
+      for (int i = 0; i < 8; ++i) {
+        const int row = 64 * wave + 8 * i + (ln >> 3);
+        const int c = (ln & 7) ^ lswz8(row);
         const int r = min(row, valid - 1);
         t.a_off[i] = (static_cast<uint32_t>(r) * static_cast<uint32_t>(K) + 8u * c) * 2u;
       }
@@ -276,41 +267,51 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
     t.ld = Nout;
   };
 
-  // direct loads of one K stage into a ring buffer, in two halves issued at
-  // different points: the token-row half (load i of 4, rows 64 wave + 16 i +
-  // lane / 4) and the weight half (load i of 4: block i / 2, step i % 2).
-  // lbw(buf): the LDS byte address of this wave's first 1 KB slot in buffer buf
-  const uint32_t lds0 = lds_addr(smem) + 4 * 1024 * wave;
-  auto lbw = [&](int buf) {
-    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds0 + static_cast<uint32_t>(buf) * kLStage));
+  // direct loads: the token rows of two K stages (a pair: 64 K values, one
+  // whole 128-byte line per row) into one of two pair buffers, load i of 8
+  // filling rows 64 wave + 8 i + lane / 8; and the weight blocks of one stage
+  // into one of four stage buffers (load i of 4: block i / 2, step i % 2).
+  // lbwA / lbwB: the LDS byte address of this wave's first 1 KB slot
+  const uint32_t lds0 = lds_addr(smem);
+  auto lbwA = [&](int pbuf) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+        lds0 + static_cast<uint32_t>(pbuf) * kLPairA + 8192u * static_cast<uint32_t>(wave)));
+  };
+  auto lbwB = [&](int buf) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+        lds0 + kLBOff + static_cast<uint32_t>(buf) * kLStageB + 4096u * static_cast<uint32_t>(wave)));
   };
   const uint32_t vb[2] = {static_cast<uint32_t>(lane) * 16u, static_cast<uint32_t>(lane) * 16u + 1024u};
-  auto issue_a = [&](const unsigned char* src, const uint32_t (&aoff)[4], uint32_t lb, int i) __attribute__((always_inline)) {
+  auto issue_a = [&](const unsigned char* src, const uint32_t (&aoff)[8], uint32_t lb, int i) __attribute__((always_inline)) {
     switch (i) {
       case 0: dma_lds<0>(src, aoff[0], lb); break;
       case 1: dma_lds<1024>(src, aoff[1], lb); break;
       case 2: dma_lds<2048>(src, aoff[2], lb); break;
-      default: dma_lds<3072>(src, aoff[3], lb); break;
+      case 3: dma_lds<3072>(src, aoff[3], lb); break;
+      case 4: dma_lds<4096>(src, aoff[4], lb); break;
+      case 5: dma_lds<5120>(src, aoff[5], lb); break;
+      case 6: dma_lds<6144>(src, aoff[6], lb); break;
+      default: dma_lds<7168>(src, aoff[7], lb); break;
     }
   };
   auto issue_b = [&](const unsigned char* w0, const unsigned char* w1, uint32_t lb, int i) __attribute__((always_inline)) {
     switch (i) {
-      case 0: dma_lds<kLStageA>(w0, vb[0], lb); break;
-      case 1: dma_lds<kLStageA + 1024>(w0, vb[1], lb); break;
-      case 2: dma_lds<kLStageA + 2048>(w1, vb[0], lb); break;
-      default: dma_lds<kLStageA + 3072>(w1, vb[1], lb); break;
+      case 0: dma_lds<0>(w0, vb[0], lb); break;
+      case 1: dma_lds<1024>(w0, vb[1], lb); break;
+      case 2: dma_lds<2048>(w1, vb[0], lb); break;
+      default: dma_lds<3072>(w1, vb[1], lb); break;
     }
   };
-  auto issue_a_all = [&](const LTile& t, int kb, int buf) {
-    const unsigned char* src = uni(t.a + 64 * kb);
+  auto issue_a_all = [&](const LTile& t, int q, int pbuf) {
+    const unsigned char* src = uni(t.a + 128 * q);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) issue_a(src, t.a_off, lbw(buf), i);
+    for (int i = 0; i < 8; ++i) issue_a(src, t.a_off, lbwA(pbuf), i);
   };
   auto issue_b_all = [&](const LTile& t, int kb, int buf) {
     const unsigned char* w0 = uni(t.w[0] + 2048 * kb);
     const unsigned char* w1 = uni(t.w[1] + 2048 * kb);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) issue_b(w0, w1, lbw(buf), i);
+    for (int i = 0; i < 4; ++i) issue_b(w0, w1, lbwB(buf), i);
   };
 
   // Token ids of a gathered tile: one direct load of 4 bytes per lane puts the
@@ -329,37 +330,44 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
                  : "memory", "m0");
   };
   // the row offsets of a gathered tile from its ids in LDS (once its load
-  // has landed): load i, lane l reads row 64 wave + 16 i + l / 4
+  // has landed): load i, lane l reads row 64 wave + 8 i + l / 8
   auto ids_offsets = [&](LTile& t) __attribute__((always_inline)) {
     if (!t.gathered) return;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 64 * wave + 16 * i + (lane >> 2);
-      const int tok = min(max(ids_lds[wave][16 * i + (lane >> 2)], 0), g.T - 1);
-      const int c = (lane & 3) ^ lswz(row);
+    for (int i = 0; i < 8; ++i) {
+      const int row = 64 * wave + 8 * i + (lane >> 3);
+      const int tok = min(max(ids_lds[wave][8 * i + (lane >> 3)], 0), g.T - 1);
+      const int c = (lane & 7) ^ lswz8(row);
       t.a_off[i] = (static_cast<uint32_t>(tok) * static_cast<uint32_t>(t.K) + 8u * c) * 2u;
     }
   };
 
   // LDS byte offsets of this lane's operand chunks: token row (lane mod 32) of
-  // a block, chunk 2 step + lane / 32; weight block at 1 KB per (block, step)
+  // a block, chunk 4 par + 2 step + lane / 32 of its pair's 8 (par: the
+  // stage's place in its pair); weight block at 1 KB per (block, step)
   const int ar = lane & 31;
-  const uint32_t a_lane[2] = {static_cast<uint32_t>(64 * ar + 16 * ((0 + (lane >> 5)) ^ lswz(ar))),
-                              static_cast<uint32_t>(64 * ar + 16 * ((2 + (lane >> 5)) ^ lswz(ar)))};
+  uint32_t a_lane[2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+      a_lane[par][st] = static_cast<uint32_t>(128 * ar + 16 * ((4 * par + 2 * st + (lane >> 5)) ^ lswz8(ar)));
   // the wave's weight blocks in the tile: gate_up gate 2c, 2c + 1 and up
   // 4 + 2c, 5 + 2c; down 4c .. 4c + 3
   auto wblk = [&](int j) { return MODE == kGateUp ? (j < 2 ? 2 * wc + j : 2 + 2 * wc + j) : 4 * wc + j; };
 
   typedef bf16x8 Frag[8];           // 4 token-block operands, then 4 weight-block operands
   // operand Q of a step: Q < 4 token block Q, else weight block Q - 4
-  auto read_op = [&](int tb0, int buf, int step, int q, Frag& f) __attribute__((always_inline)) {
-    const unsigned char* s = smem + buf * kLStage;
+  // (pbuf, par: the stage's pair buffer and its place in the pair; buf: its
+  // weight buffer)
+  auto read_op = [&](int tb0, int pbuf, int par, int buf, int step, int q, Frag& f) __attribute__((always_inline)) {
     if (q < 4) {
       // (blocks past the wave's live ones are read too: in bounds, unused)
       const int tb = q == 0 ? tb0 : 2 * q + wr;
-      f[q] = *reinterpret_cast<const bf16x8*>(s + 2048 * tb + a_lane[step]);
+      f[q] = *reinterpret_cast<const bf16x8*>(smem + pbuf * kLPairA + 4096 * tb + a_lane[par][step]);
     } else {
-      f[q] = *reinterpret_cast<const bf16x8*>(s + kLStageA + (2 * wblk(q - 4) + step) * 1024 + 16 * lane);
+      f[q] = *reinterpret_cast<const bf16x8*>(smem + kLBOff + buf * kLStageB + (2 * wblk(q - 4) + step) * 1024 +
+                                              16 * lane);
     }
   };
 
@@ -370,20 +378,22 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
   ids_issue(cur, true, cur.a);
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   ids_offsets(cur);
-  int ring = 0;                      // ring buffer of the current tile's stage 0
-  // stages 0-2 and the token-row half of stage 3 (the weight half of stage
-  // x + 3 is issued in stage x's first step, the token-row half of stage
-  // x + 4 in its second)
-  for (int s = 0; s < kLNS - 1; ++s) {
-    issue_a_all(cur, s, s);
-    issue_b_all(cur, s, s);
-  }
-  issue_a_all(cur, kLNS - 1, kLNS - 1);
-  __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLLoads + kLLoads / 2));
+  int ring = 0;                      // weight buffer of the current tile's stage 0
+  int aring = 0;                     // token-row buffer of its pair 0 (stages 0 and 1)
+  // stages 0-2, in the order the previous tile's last stages issue them
+  // (weights 0, pair 0, weights 1 and 2, pair 1: the weights of stage x + 3
+  // are issued in stage x's first step, the pair of stages x + 3 and x + 4 in
+  // an odd stage x's second)
+  issue_b_all(cur, 0, 0);
+  issue_a_all(cur, 0, 0);
+  issue_b_all(cur, 1, 1);
+  issue_b_all(cur, 2, 2);
+  issue_a_all(cur, 1, 1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(16));
   __builtin_amdgcn_s_barrier();
   Frag f0, f1;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) read_op(cur.tb0, 0, 0, op_order(r), f0);
+  for (int r = 0; r < 8; ++r) read_op(cur.tb0, 0, 0, 0, 0, op_order(r), f0);
 
   bool stored = false;               // the previous tile's stores came between the token-row
                                      // and the weight halves of this tile's stage 3
@@ -395,6 +405,7 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[m][j] = f32x16{0.f};
     ring = __builtin_amdgcn_readfirstlane(ring);
+    aring = __builtin_amdgcn_readfirstlane(aring);
     const int nkb = __builtin_amdgcn_readfirstlane(cur.nkb);
     const int nv = __builtin_amdgcn_readfirstlane(cur.nv);
     // the next tile, decoded here where the accumulators hold nothing; its
@@ -425,73 +436,115 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
     };
 
     // K stage x: step 0 from f0 while reading step 1's operands into f1 and
-    // issuing the weight half of stage x + 3; barrier; step 1 from f1 while
-    // reading stage x + 1's first operands into f0 and issuing the token-row
-    // half of stage x + 4.  Stages past this tile's last are the next tile's;
-    // after the last tile they repeat this tile's first ones (in bounds,
-    // never used), so that every stage issues the same loads and waits.
-    auto stage = [&](int x, auto nv_tag) __attribute__((always_inline)) {
+    // issuing the weights of stage x + 3; barrier; step 1 from f1 while
+    // reading stage x + 1's first operands into f0 and, in an odd stage,
+    // issuing the token rows of stages x + 3 and x + 4 (one pair).  Stages
+    // past this tile's last are the next tile's; after the last tile they
+    // repeat this tile's first ones (in bounds, never used), so that every
+    // stage issues the same loads and waits.  PAR = x mod 2 (K has a multiple
+    // of 64 values, so a tile's stage count is even).
+    auto stage = [&](int x, auto par_tag, auto nv_tag) __attribute__((always_inline)) {
+      constexpr int PAR = decltype(par_tag)::value;
       const int b0 = (ring + x) & (kLNS - 1);
       const int b1 = (b0 + 1) & (kLNS - 1);
       const int b3 = (b0 + kLNS - 1) & (kLNS - 1);
-      const uint32_t l3 = lbw(b3), l0 = lbw(b0);
+      const int p0 = (aring + (x >> 1)) & 1;           // stage x's token-row buffer
+      const int p1 = PAR ? p0 ^ 1 : p0;                // stage x + 1's
+      const uint32_t l3 = lbwB(b3);
       const bool wnx = x + 3 >= nkb;
       const int wk = wnx ? x + 3 - nkb : x + 3;
       const unsigned char* w0 = uni((wnx ? nxt.w[0] : cur.w[0]) + 2048 * wk);
       const unsigned char* w1 = uni((wnx ? nxt.w[1] : cur.w[1]) + 2048 * wk);
-      // the next tile's row offsets, before its first load (step 1 of stage
-      // nkb - 4); its ids landed by stage 2's wait (nkb >= 8)
+      // the next tile's row offsets, before its first token-row load (step 1
+      // of stage nkb - 3); its ids landed by stage 2's wait (nkb >= 8)
       if (x == nkb - kLNS && has_next) ids_offsets(nxt);
       step(f0, nv_tag, [&](int k) __attribute__((always_inline)) {
-        if ((k & 1) == 0) read_op(cur.tb0, b0, 1, op_order(k >> 1), f1);
+        if ((k & 1) == 0) read_op(cur.tb0, p0, PAR, b0, 1, op_order(k >> 1), f1);
         else if ((k & 3) == 1) issue_b(w0, w1, l3, k >> 2);
       });
-      // after stage x + 1's last load came both halves of stages x + 2 and
-      // x + 3 and, for stages 0 and 1, the next tile's id load and the
-      // previous tile's stores
-      if (x <= 1) {
-        if (stored) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLLoads + 1 + kStores));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLLoads + 1));
+      // stage x + 1 has landed once no more than the loads issued after its
+      // last one are outstanding: even x, the weights of stages x + 2 and
+      // x + 3 and the pair of x + 3, x + 4 (16); odd x, the weights of x + 2
+      // and x + 3 (8); stages 0 and 1 also count the next tile's id load and
+      // the previous tile's stores
+      if constexpr (PAR == 0) {
+        if (x == 0) {
+          if (stored) __builtin_amdgcn_s_waitcnt(vmcnt_only(17 + kStores));
+          else __builtin_amdgcn_s_waitcnt(vmcnt_only(17));
+        } else {
+          __builtin_amdgcn_s_waitcnt(vmcnt_only(16));
+        }
       } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLLoads));
+        if (x == 1) {
+          if (stored) __builtin_amdgcn_s_waitcnt(vmcnt_only(9 + kStores));
+          else __builtin_amdgcn_s_waitcnt(vmcnt_only(9));
+        } else {
+          __builtin_amdgcn_s_waitcnt(vmcnt_only(8));
+        }
       }
-      // every wave's reads of stage x were issued in its first step: done
-      // before the barrier hands the buffer to stage x + 4
+      // every wave's reads of stage x were issued by its first step: done
+      // before the barrier hands its buffers on
       __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
       __builtin_amdgcn_s_barrier();
-      const bool anx = x + 4 >= nkb;
-      const int ak = anx ? x + 4 - nkb : x + 4;
-      const unsigned char* asrc = uni((anx ? nxt.a : cur.a) + 64 * ak);
-      uint32_t aoff[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) aoff[i] = anx ? nxt.a_off[i] : cur.a_off[i];
       const int tb0 = x + 1 >= nkb ? nxt.tb0 : cur.tb0;
-      step(f1, nv_tag, [&](int k) __attribute__((always_inline)) {
-        if ((k & 1) == 0) read_op(tb0, b1, 0, op_order(k >> 1), f0);
-        else if ((k & 3) == 1) issue_a(asrc, aoff, l0, k >> 2);
-      });
+      if constexpr (PAR == 1) {
+        // the pair of stages x + 3, x + 4 goes where stages x - 1, x were
+        const int q = (x + 3) >> 1;
+        const bool anx = q >= (nkb >> 1);
+        const int aq = anx ? q - (nkb >> 1) : q;
+        const unsigned char* asrc = uni((anx ? nxt.a : cur.a) + 128 * aq);
+        uint32_t aoff[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) aoff[i] = anx ? nxt.a_off[i] : cur.a_off[i];
+        const uint32_t la = lbwA(p0);
+        step(f1, nv_tag, [&](int k) __attribute__((always_inline)) {
+          if ((k & 1) == 0) read_op(tb0, p1, 0, b1, 0, op_order(k >> 1), f0);
+          else issue_a(asrc, aoff, la, k >> 1);
+        });
+      } else {
+        step(f1, nv_tag, [&](int k) __attribute__((always_inline)) {
+          if ((k & 1) == 0) read_op(tb0, p1, 1, b1, 0, op_order(k >> 1), f0);
+        });
+      }
     };
 
-    // stages whose loads all come from this tile and whose waits count no
-    // stores: the same work from pointers advanced once per stage
+    // two stages x, x + 1 (x even) whose loads all come from this tile and
+    // whose waits count no stores: the same work from pointers advanced once
+    // per stage
     auto fast = [&](int x, const unsigned char*& pa, const unsigned char*& pw0, const unsigned char*& pw1,
                     auto nv_tag) __attribute__((always_inline)) {
       const int b0 = (ring + x) & (kLNS - 1);
       const int b1 = (b0 + 1) & (kLNS - 1);
+      const int b2 = (b0 + 2) & (kLNS - 1);
       const int b3 = (b0 + kLNS - 1) & (kLNS - 1);
-      const uint32_t l3 = lbw(b3), l0 = lbw(b0);
+      const int p0 = (aring + (x >> 1)) & 1;
+      const uint32_t l3 = lbwB(b3);
       step(f0, nv_tag, [&](int k) __attribute__((always_inline)) {
-        if ((k & 1) == 0) read_op(cur.tb0, b0, 1, op_order(k >> 1), f1);
+        if ((k & 1) == 0) read_op(cur.tb0, p0, 0, b0, 1, op_order(k >> 1), f1);
         else if ((k & 3) == 1) issue_b(pw0, pw1, l3, k >> 2);
       });
-      wait_vm<kStores>(2, false);
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(16));
       __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
       __builtin_amdgcn_s_barrier();
       step(f1, nv_tag, [&](int k) __attribute__((always_inline)) {
-        if ((k & 1) == 0) read_op(cur.tb0, b1, 0, op_order(k >> 1), f0);
-        else if ((k & 3) == 1) issue_a(pa, cur.a_off, l0, k >> 2);
+        if ((k & 1) == 0) read_op(cur.tb0, p0, 1, b1, 0, op_order(k >> 1), f0);
       });
-      pa += 64;
+      pw0 += 2048;
+      pw1 += 2048;
+      const uint32_t l0 = lbwB(b0);
+      step(f0, nv_tag, [&](int k) __attribute__((always_inline)) {
+        if ((k & 1) == 0) read_op(cur.tb0, p0, 1, b1, 1, op_order(k >> 1), f1);
+        else if ((k & 3) == 1) issue_b(pw0, pw1, l0, k >> 2);
+      });
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(8));
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+      __builtin_amdgcn_s_barrier();
+      const uint32_t la = lbwA(p0);
+      step(f1, nv_tag, [&](int k) __attribute__((always_inline)) {
+        if ((k & 1) == 0) read_op(cur.tb0, p0 ^ 1, 0, b2, 0, op_order(k >> 1), f0);
+        else issue_a(pa, cur.a_off, la, k >> 1);
+      });
+      pa += 128;
       pw0 += 2048;
       pw1 += 2048;
     };
@@ -501,14 +554,18 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
     // the previous tile's stores) and the last four (the next tile's loads)
     // take the general body, the others the fast one
     auto k_loop = [&](auto nv_tag) __attribute__((always_inline)) {
-      stage(0, nv_tag);
-      stage(1, nv_tag);
-      const int tail = max(2, nkb - kLNS);
-      const unsigned char* pa = uni(cur.a + 64 * (2 + kLNS));
-      const unsigned char* pw0 = uni(cur.w[0] + 2048 * (2 + kLNS - 1));
-      const unsigned char* pw1 = uni(cur.w[1] + 2048 * (2 + kLNS - 1));
-      for (int x = 2; x < tail; ++x) fast(x, pa, pw0, pw1, nv_tag);
-      for (int x = tail; x < nkb; ++x) stage(x, nv_tag);
+      using P0 = std::integral_constant<int, 0>;
+      using P1 = std::integral_constant<int, 1>;
+      stage(0, P0{}, nv_tag);
+      stage(1, P1{}, nv_tag);
+      const unsigned char* pa = uni(cur.a + 128 * 3);
+      const unsigned char* pw0 = uni(cur.w[0] + 2048 * 5);
+      const unsigned char* pw1 = uni(cur.w[1] + 2048 * 5);
+      for (int x = 2; x < nkb - kLNS; x += 2) fast(x, pa, pw0, pw1, nv_tag);
+      stage(nkb - 4, P0{}, nv_tag);
+      stage(nkb - 3, P1{}, nv_tag);
+      stage(nkb - 2, P0{}, nv_tag);
+      stage(nkb - 1, P1{}, nv_tag);
     };
     // ---- epilogue: round, pack and store.  Lane l holds token l mod 32 of a
     // block and columns 8q + 4 (l / 32) + 0..3 (q = 0..3) of a 32-column
@@ -531,7 +588,7 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
       constexpr int NV = decltype(nv_tag)::value;
       constexpr int kHalves = kJ / 2;                // 64-column pieces of the wave's columns
       const LTile& o = cur;
-      unsigned char* stg = smem + ((ring + nkb - 1) & (kLNS - 1)) * kLStage + kLStageA + wave * 4096;
+      unsigned char* stg = smem + kLBOff + ((ring + nkb - 1) & (kLNS - 1)) * kLStageB + wave * 4096;
       u32x4 first[NV < 4 ? kHalves : 1][4];
       typedef __attribute__((address_space(1))) unsigned char gbyte;
       typedef __attribute__((address_space(1))) u32x4 gu32x4;
@@ -628,6 +685,7 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
 
     stored = true;
     ring = (ring + nkb) & (kLNS - 1);
+    aring = (aring + (nkb >> 1)) & 1;
     ++round;
     ti = tn;
     if (has_next) cur = nxt;
@@ -642,8 +700,8 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
 bool lds_gemm_fits(int mode, const GemmArgs& a) {
   const int cols = mode == kGateUp ? kLBN / 2 : kLBN;
   if (a.E > kGemmMaxE) return false;
-  if (a.E > 0 && (a.K % kLBK != 0 || a.K < 8 * kLBK || a.N % cols != 0)) return false;
-  if (a.has_shared && (a.Ks % kLBK != 0 || a.Ks < 8 * kLBK || a.Ns % cols != 0)) return false;
+  if (a.E > 0 && (a.K % (2 * kLBK) != 0 || a.K < 8 * kLBK || a.N % cols != 0)) return false;
+  if (a.has_shared && (a.Ks % (2 * kLBK) != 0 || a.Ks < 8 * kLBK || a.Ns % cols != 0)) return false;
   return true;
 }
 
