@@ -67,14 +67,16 @@ GEMM_SOURCES = ("grouped_gemm.hip", "grouped_gemm_lds.hip", "grouped_gemm.h", "m
                 "moe_internal.h")
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
-    "prefill_outlier_bf16_t32768_d2048": (1909411.2, 295873.7,
-                                          "dba5674429f905e79f0f6d19a472947b65ed6f172fe252ed82d1e91f37837114"),
-    "xs2_bf16_t4096_d2048": (656867.2, 36864.2,
-                             "dba5674429f905e79f0f6d19a472947b65ed6f172fe252ed82d1e91f37837114"),
-    "m1_bf16_t8192_d4096": (3256389.4, 147458.4,
-                            "dba5674429f905e79f0f6d19a472947b65ed6f172fe252ed82d1e91f37837114"),
-    "decode_zipf_bf16_t32_d4096": (493913.0, 576.0,
-                                   "dba5674429f905e79f0f6d19a472947b65ed6f172fe252ed82d1e91f37837114"),
+    "prefill_outlier_bf16_t32768_d2048": (2209400.9, 296499.0,
+                                          "9d5b425592dc8546f5d4acbfaf7ca0a219123a3bb192d6a73545aec17592778f"),
+    "xs2_bf16_t4096_d2048": (658398.2, 36864.4,
+                             "9d5b425592dc8546f5d4acbfaf7ca0a219123a3bb192d6a73545aec17592778f"),
+    "m1_bf16_t8192_d4096": (3301496.4, 147592.8,
+                            "9d5b425592dc8546f5d4acbfaf7ca0a219123a3bb192d6a73545aec17592778f"),
+    "m1_top16_bf16_t8192_d4096": (5445845.3, 278867.4,
+                                  "9d5b425592dc8546f5d4acbfaf7ca0a219123a3bb192d6a73545aec17592778f"),
+    "decode_zipf_bf16_t32_d4096": (493911.0, 576.0,
+                                   "9d5b425592dc8546f5d4acbfaf7ca0a219123a3bb192d6a73545aec17592778f"),
 }
 
 

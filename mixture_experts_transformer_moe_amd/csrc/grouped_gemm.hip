@@ -443,13 +443,11 @@ hipError_t launch_tiles(const GemmArgs& a, int mean_rows, hipStream_t st) {
   constexpr int P = W8 ? 8 : 16;
   const int wide = MODE == kGateUp ? 256 : 512;            // output columns of an NB = 4 tile
   // The LDS-tiled kernel (256 x 256 tiles, both operands through LDS) beats
-  // the weight-streaming tiles below once most of an expert's rows sit in full
-  // 256-row tiles. Measured: the down projection (K = F) from 256 rows per
-  // expert on (7% faster at 256 and at 512, 11% at 1024); the gate/up
-  // projection (K = D) only at 1024 (11% faster; 1-2% slower at 256 and 512,
-  // where the short last row tile of each expert streams a full 256 x D slice
-  // of weights for few rows)
-  const int lds_from = MODE == kDown ? 256 : 768;
+  // the weight-streaming tiles below once an expert has a full 256-row tile
+  // on average.  Measured (D = 4096, F = 1024 and D = 2048, F = 512): down
+  // 7-11% faster at 256, 512 and 1024 rows per expert; gate/up 3% faster at
+  // 256 and 512, 11% at 1024
+  const int lds_from = 256;
   if (!W8 && mean_rows >= lds_from && lds_gemm_fits(MODE, a)) return launch_lds_gemm(MODE, a, st);
   if (mean_rows >= 192 && a.N % wide == 0 && (!a.has_shared || a.Ns % wide == 0))
     grouped_gemm_kernel<MODE, 96, 4, 8, W8><<<persistent_grid(), kThreads, 0, st>>>(a);
