@@ -67,16 +67,16 @@ GEMM_SOURCES = ("grouped_gemm.hip", "grouped_gemm_lds.hip", "grouped_gemm.h", "m
                 "moe_internal.h")
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
-    "prefill_outlier_bf16_t32768_d2048": (2209400.9, 296499.0,
-                                          "9d5b425592dc8546f5d4acbfaf7ca0a219123a3bb192d6a73545aec17592778f"),
-    "xs2_bf16_t4096_d2048": (658398.2, 36864.4,
-                             "9d5b425592dc8546f5d4acbfaf7ca0a219123a3bb192d6a73545aec17592778f"),
-    "m1_bf16_t8192_d4096": (3301496.4, 147592.8,
-                            "9d5b425592dc8546f5d4acbfaf7ca0a219123a3bb192d6a73545aec17592778f"),
-    "m1_top16_bf16_t8192_d4096": (5445845.3, 278867.4,
-                                  "9d5b425592dc8546f5d4acbfaf7ca0a219123a3bb192d6a73545aec17592778f"),
-    "decode_zipf_bf16_t32_d4096": (493911.0, 576.0,
-                                   "9d5b425592dc8546f5d4acbfaf7ca0a219123a3bb192d6a73545aec17592778f"),
+    "prefill_outlier_bf16_t32768_d2048": (2220334.4, 296593.7,
+                                          "a96b28553c4bbd8370921cffac36f3f4b049b73820a753307f5bbd8254a65a6f"),
+    "xs2_bf16_t4096_d2048": (657312.4, 36864.3,
+                             "a96b28553c4bbd8370921cffac36f3f4b049b73820a753307f5bbd8254a65a6f"),
+    "m1_bf16_t8192_d4096": (3305043.9, 147597.8,
+                            "a96b28553c4bbd8370921cffac36f3f4b049b73820a753307f5bbd8254a65a6f"),
+    "m1_top16_bf16_t8192_d4096": (5444833.1, 278859.4,
+                                  "a96b28553c4bbd8370921cffac36f3f4b049b73820a753307f5bbd8254a65a6f"),
+    "decode_zipf_bf16_t32_d4096": (493915.0, 576.0,
+                                   "a96b28553c4bbd8370921cffac36f3f4b049b73820a753307f5bbd8254a65a6f"),
 }
 
 

@@ -196,12 +196,14 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
     return base + xcd * q + min(xcd, rem) + in_xcd;
   };
 
-  // ---- sources and output of schedule slot ti
-  auto decode = [&](int ti, LTile& t) __attribute__((always_inline)) {
-    int ln = tid & 63;
-    asm volatile("" : "+v"(ln));      // per-lane arithmetic stays inside decode
+  // ---- where a tile sits: group (E: the shared expert), its first row and
+  // row count, the tile's origin
+  struct Where {
+    int grp, rb, M, m0, n0;
+  };
+  auto locate = [&](int ti) __attribute__((always_inline)) {
     const bool shared = ti < n_sh;
-    int grp = E, local = ti, first = 0;
+    int grp = E, local = ti;
     if (!shared) {
       const int r = ti - n_sh;
       int lo = 0, hi = E - 1;         // first group with tile_end > r
@@ -209,15 +211,74 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
         const int mid = (lo + hi) >> 1;
         if (tile_end[mid] > r) hi = mid; else lo = mid + 1;
       }
-      grp = __builtin_amdgcn_readfirstlane(lo);
-      first = grp == 0 ? 0 : __builtin_amdgcn_readfirstlane(tile_end[grp - 1]);
-      local = r - first;
+      grp = lo;
+      local = r - (grp == 0 ? 0 : tile_end[grp - 1]);
     }
-    const int rb = shared ? 0 : __builtin_amdgcn_readfirstlane(row_base[grp]);
-    const int M = shared ? g.T : __builtin_amdgcn_readfirstlane(row_base[grp + 1]) - rb;
-    const int nt = shared ? nt_s : nt_r;
-    const int m0 = (local / nt) * kLBM;
-    const int n0 = (local % nt) * kOutCols;
+    const int nt = max(1, shared ? nt_s : nt_r);
+    local = max(local, 0);
+    Where w;
+    w.grp = grp;
+    w.rb = shared ? 0 : row_base[grp];
+    w.M = shared ? g.T : row_base[grp + 1] - w.rb;
+    w.m0 = (local / nt) * kLBM;
+    w.n0 = (local % nt) * kOutCols;
+    return w;
+  };
+  // The down projection's tiles are short (K = F), so walking the tile table
+  // for each one (a chain of dependent LDS and scalar loads at the tile top)
+  // weighs more there: lane l of each wave locates the tile of round r0 + l,
+  // 64 rounds at a time, and a tile's decode reads its entry with v_readlane
+  // (d_grp -1: no tile; measured: down 1-2% faster on the long prefill and at
+  // the M.1 widths, results bit for bit the same).  Gate/up (K = D, 4x longer
+  // tiles) walks the table per tile: the batch's registers made it 1% slower.
+  constexpr bool kBatch = MODE == kDown;
+  int d_grp = 0, d_rb = 0, d_M = 0, d_m0 = 0, d_n0 = 0;
+  auto fill_batch = [&](int r0) {
+    const int ti = tile_at(r0 + lane);
+    const Where w = locate(max(ti, 0));
+    d_grp = ti < 0 ? -1 : w.grp;
+    d_rb = w.rb;
+    d_M = w.M;
+    d_m0 = w.m0;
+    d_n0 = w.n0;
+  };
+
+  // ---- sources and output of the tile of round r (slot ti)
+  auto decode = [&](int r, int ti, LTile& t) __attribute__((always_inline)) {
+    int ln = tid & 63;
+    asm volatile("" : "+v"(ln));      // per-lane arithmetic stays inside decode
+    int grp, rb, M, m0, n0;
+    bool shared;
+    if constexpr (kBatch) {
+      const int sl = r & 63;
+      grp = __builtin_amdgcn_readlane(d_grp, sl);
+      shared = grp == E;
+      rb = __builtin_amdgcn_readlane(d_rb, sl);
+      M = __builtin_amdgcn_readlane(d_M, sl);
+      m0 = __builtin_amdgcn_readlane(d_m0, sl);
+      n0 = __builtin_amdgcn_readlane(d_n0, sl);
+    } else {
+      const bool sh = ti < n_sh;
+      shared = sh;
+      int local = ti, first = 0;
+      grp = E;
+      if (!sh) {
+        const int r = ti - n_sh;
+        int lo = 0, hi = E - 1;       // first group with tile_end > r
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (tile_end[mid] > r) hi = mid; else lo = mid + 1;
+        }
+        grp = __builtin_amdgcn_readfirstlane(lo);
+        first = grp == 0 ? 0 : __builtin_amdgcn_readfirstlane(tile_end[grp - 1]);
+        local = r - first;
+      }
+      rb = sh ? 0 : __builtin_amdgcn_readfirstlane(row_base[grp]);
+      M = sh ? g.T : __builtin_amdgcn_readfirstlane(row_base[grp + 1]) - rb;
+      const int nt = sh ? nt_s : nt_r;
+      m0 = (local / nt) * kLBM;
+      n0 = (local % nt) * kOutCols;
+    }
     const int K = shared ? g.Ks : g.K;
     const int Nout = shared ? g.Ns : g.N;
     const int valid = min(kLBM, M - m0);
@@ -371,10 +432,11 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
     }
   };
 
+  if constexpr (kBatch) fill_batch(0);
   const int pos = tile_at(0);
   if (pos < 0) return;
   LTile cur, nxt;
-  decode(pos, cur);
+  decode(0, pos, cur);
   ids_issue(cur, true, cur.a);
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   ids_offsets(cur);
@@ -411,9 +473,12 @@ __global__ __launch_bounds__(kLThreads, 1) void lds_gemm_kernel(GemmArgs g) {
     // the next tile, decoded here where the accumulators hold nothing; its
     // token ids land in LDS behind this tile's first loads (the waits of
     // stages 0 and 1 count the one load, and stage 2's wait covers it)
+    if constexpr (kBatch) {
+      if (((round + 1) & 63) == 0) fill_batch(round + 1);
+    }
     const int tn = tile_at(round + 1);
     const bool has_next = tn >= 0;
-    if (has_next) decode(tn, nxt);
+    if (has_next) decode(round + 1, tn, nxt);
     else nxt = cur;
     ids_issue(nxt, has_next, cur.a);
 

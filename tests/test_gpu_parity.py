@@ -203,6 +203,37 @@ def test_nan_in_one_token_stays_in_that_token(shape):
                        b.sorted_token.cpu().numpy(), b.slot_of.cpu().numpy(), s.E)
 
 
+def test_router_large_batch_with_padding_mask():
+    """The router's largest block shape (all 256 experts of 128 tokens per
+    workgroup) with a padding mask and a ragged last block (32700 tokens):
+    logits within 1e-5 max|z| of fp64, every token's experts bit-exact against
+    the oracle's selection on the GPU's fp32 logits, weights within 1e-6,
+    padding tokens expert -1 and weight 0."""
+    from oracle import train_oracle as TR
+    from mixture_experts_transformer_moe_amd.inputs import token_mask
+    s = configs.variant(SMALL_BF16, name="router_mask_t32700", T=32700, D=256, E=256, k=8, F=256, Fs=256,
+                        pad_frac=0.1, seq_len=700, seed=41)
+    assert s.E == 256 and (s.T + 127) // 128 >= 256 and s.T % 128 != 0
+    inp = LayerInputs(s)
+    x, w = binding.upload(inp)
+    mask = token_mask(s)
+    n_pad = int((mask == 0).sum())
+    assert 0 < n_pad < s.T
+    b = binding.alloc_buffers(s, with_x_perm=False)
+    c = binding.make_shape(s)
+    binding.moe_route_masked(c, x, w.w_router, w.bias, torch.from_numpy(mask).cuda(), b.logits, b.topk_idx,
+                             b.topk_w)
+    torch.cuda.synchronize()
+    logits = b.logits.cpu().numpy()
+    z64 = O.router_logits(inp.x, inp.w_router, inp.bias)
+    err = np.abs(logits.astype(np.float64) - z64).max()
+    assert err <= 1e-5 * np.abs(z64).max(), f"logit error {err}"
+    r = TR.route_masked(logits.astype(np.float64), s.k, mask)
+    assert np.array_equal(b.topk_idx.cpu().numpy(), r.topk_idx), "topk_idx differs"
+    np.testing.assert_allclose(b.topk_w.cpu().numpy(), r.topk_w, rtol=1e-6, atol=0)
+    say(f"{s.name}: {n_pad} padding tokens, routing bit-exact")
+
+
 # ------------------------------------------------------------------ edge cases
 
 EDGE = {
