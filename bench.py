@@ -68,15 +68,15 @@ GEMM_SOURCES = ("grouped_gemm.hip", "grouped_gemm_lds.hip", "grouped_gemm.h", "m
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
     "prefill_outlier_bf16_t32768_d2048": (2220334.4, 296593.7,
-                                          "a96b28553c4bbd8370921cffac36f3f4b049b73820a753307f5bbd8254a65a6f"),
+                                          "ab9df5d4c1f7274e6ef5aab1e1332914ef1b201fdb6f0537880ff0dead8e2dad"),
     "xs2_bf16_t4096_d2048": (657312.4, 36864.3,
-                             "a96b28553c4bbd8370921cffac36f3f4b049b73820a753307f5bbd8254a65a6f"),
+                             "ab9df5d4c1f7274e6ef5aab1e1332914ef1b201fdb6f0537880ff0dead8e2dad"),
     "m1_bf16_t8192_d4096": (3305043.9, 147597.8,
-                            "a96b28553c4bbd8370921cffac36f3f4b049b73820a753307f5bbd8254a65a6f"),
+                            "ab9df5d4c1f7274e6ef5aab1e1332914ef1b201fdb6f0537880ff0dead8e2dad"),
     "m1_top16_bf16_t8192_d4096": (5444833.1, 278859.4,
-                                  "a96b28553c4bbd8370921cffac36f3f4b049b73820a753307f5bbd8254a65a6f"),
+                                  "ab9df5d4c1f7274e6ef5aab1e1332914ef1b201fdb6f0537880ff0dead8e2dad"),
     "decode_zipf_bf16_t32_d4096": (493915.0, 576.0,
-                                   "a96b28553c4bbd8370921cffac36f3f4b049b73820a753307f5bbd8254a65a6f"),
+                                   "ab9df5d4c1f7274e6ef5aab1e1332914ef1b201fdb6f0537880ff0dead8e2dad"),
 }
 
 

@@ -35,7 +35,7 @@ struct GemmArgs {
 int persistent_grid();
 
 // The LDS-tiled kernel: 256 x 256 tiles (gate/up: 128 output columns), bf16
-// weights, K and Ks multiples of 32 and at least 128, N and Ns multiples of
+// weights, K and Ks multiples of 64 and at least 256, N and Ns multiples of
 // the tile's output columns.
 bool lds_gemm_fits(int mode, const GemmArgs& a);
 hipError_t launch_lds_gemm(int mode, const GemmArgs& a, hipStream_t st);

@@ -158,6 +158,21 @@ def test_prefill_outlier_workload_parity():
     sampled_parity(configs.PREFILL_OUTLIER_T32768, n_tokens=256, all_outliers=True, expert_rows=6)
 
 
+def test_lds_tiled_many_rounds_sampled_parity():
+    """A down launch whose workgroups each run more than 64 tiles (the down
+    kernel locates its tiles 64 rounds at a time): 32768 tokens to all 8
+    experts, D = 4096 (16 column tiles per 256-row block), F = 256 (the
+    shortest K the LDS-tiled kernel takes: 8 stages): 1152 row blocks x 16 =
+    18432 tiles, 72 per workgroup on 256 CUs."""
+    s = configs.variant(SMALL_BF16, name="lds_rounds_t32768_e8_d4096", T=32768, D=4096, E=8, k=8, F=256,
+                        Fs=256, seed=43)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = (cus + 7) // 8 * 8
+    row_blocks = s.E * ((s.T * s.k // s.E + 255) // 256) + (s.T + 255) // 256
+    assert row_blocks * (s.D // 256) > 64 * grid
+    sampled_parity(s, n_tokens=64, expert_rows=2)
+
+
 @pytest.mark.parametrize("name", [configs.M1_T8192.name, configs.M1_TOP16_T8192.name])
 def test_m1_width_workload_sampled_parity(name):
     sampled_parity(configs.get(name), n_tokens=256, expert_rows=4)
