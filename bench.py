@@ -68,15 +68,15 @@ GEMM_SOURCES = ("grouped_gemm.hip", "grouped_gemm_lds.hip", "grouped_gemm.h", "m
 TRAFFIC = {
     # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of GEMM_SOURCES)
     "prefill_outlier_bf16_t32768_d2048": (2220334.4, 296593.7,
-                                          "ab9df5d4c1f7274e6ef5aab1e1332914ef1b201fdb6f0537880ff0dead8e2dad"),
+                                          "7a444bd95cd2e0f0d71c371dd3d20d23890a983b340c180b63e9797b254bd5ef"),
     "xs2_bf16_t4096_d2048": (657312.4, 36864.3,
-                             "ab9df5d4c1f7274e6ef5aab1e1332914ef1b201fdb6f0537880ff0dead8e2dad"),
+                             "7a444bd95cd2e0f0d71c371dd3d20d23890a983b340c180b63e9797b254bd5ef"),
     "m1_bf16_t8192_d4096": (3305043.9, 147597.8,
-                            "ab9df5d4c1f7274e6ef5aab1e1332914ef1b201fdb6f0537880ff0dead8e2dad"),
+                            "7a444bd95cd2e0f0d71c371dd3d20d23890a983b340c180b63e9797b254bd5ef"),
     "m1_top16_bf16_t8192_d4096": (5444833.1, 278859.4,
-                                  "ab9df5d4c1f7274e6ef5aab1e1332914ef1b201fdb6f0537880ff0dead8e2dad"),
+                                  "7a444bd95cd2e0f0d71c371dd3d20d23890a983b340c180b63e9797b254bd5ef"),
     "decode_zipf_bf16_t32_d4096": (493915.0, 576.0,
-                                   "ab9df5d4c1f7274e6ef5aab1e1332914ef1b201fdb6f0537880ff0dead8e2dad"),
+                                   "7a444bd95cd2e0f0d71c371dd3d20d23890a983b340c180b63e9797b254bd5ef"),
 }
 
 

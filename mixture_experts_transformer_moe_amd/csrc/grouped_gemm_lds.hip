@@ -66,7 +66,7 @@ constexpr int kLThreads = 256;
 constexpr int kLBM = 256;                 // token rows per tile
 constexpr int kLBN = 256;                 // weight rows per tile
 constexpr int kLBK = 32;                  // K per LDS stage (two 16-wide MFMA steps)
-constexpr int kLNS = 4;                   // LDS stages
+constexpr int kLNS = 4;                   // weight buffers of the ring (one K stage each)
 constexpr int kLPairA = kLBM * 2 * kLBK * 2;   // 32 KB: token rows of two K stages (128 bytes a row)
 constexpr int kLStageB = kLBN * kLBK * 2;      // 16 KB of weight blocks per stage
 constexpr int kLBOff = 2 * kLPairA;            // the weight ring follows the two token-row pair buffers
@@ -84,22 +84,10 @@ constexpr int lgkmcnt_only(int n) { return 15 | (7 << 4) | ((n & 15) << 8) | (3 
 // weight blocks 0-3, token blocks 1-3): read r of a step fetches operand
 // op_order(r).
 constexpr int op_order(int r) { return r == 0 ? 0 : (r <= 4 ? 3 + r : r - 4); }
-template <int R>
-using OpAt = std::integral_constant<int, op_order(R)>;
-
-// f(integral_constant<int, I>) for I = 0 .. N - 1, unrolled at compile time.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 // Sources of one tile (everything uniform except a_off).
 struct LTile {
-  const unsigned char* a;      // token rows: the chunk of load i of K stage kb is at a + 64 kb + a_off[i]
+  const unsigned char* a;      // token rows: the chunk of load i of pair q (K stages 2q, 2q + 1) is at a + 128 q + a_off[i]
   uint32_t a_off[8];
   const unsigned char* w[2];   // the wave's two weight blocks: K stage kb, step s at w[j] + 2048 kb + 1024 s
   int nkb;                     // K / 32
