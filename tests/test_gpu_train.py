@@ -311,4 +311,22 @@ def test_m1_width_training_sampled_parity():
     x = O.widen(inp.x)
     dz16 = to_f64(b.dz16)[:, :s.E]
     assert_close_rel(b.dw_router.cpu().numpy().astype(np.float64), dz16.T @ x, 1e-3, "dw_router = dz^T x")
+    # one expert's router-gradient row and bias entry against the oracle's own
+    # dz column: the tokens routed to the expert take their whole dz rows (the
+    # top-k weights' path through all their experts, and the auxiliary loss),
+    # every other real token only the auxiliary-loss term, padding none
+    e = int(np.argmax(r.counts))
+    toks_e = r.sorted_token[r.offsets[e]:r.offsets[e + 1]]
+    say(f"oracle dz column of expert {e}: {len(toks_e)} routed tokens in full, the rest through the aux loss")
+    dz_rows, _ = TR.token_grads(inp, s.alpha, r, dout, toks_e, s.aux_coef)
+    col = np.zeros(s.T)
+    c = TR.aux_coefficients(r, s.aux_coef)
+    assert c is not None
+    real = r.topk_idx[:, 0] >= 0
+    sig = TR.sigmoid(r.logits)
+    col[real] = (TR.aux_dsigma(sig, c) * sig * (1.0 - sig))[real, e]
+    col[toks_e] = dz_rows[:, e]
+    assert_close_rel(b.dw_router.cpu().numpy()[e].astype(np.float64), col @ x, TOL,
+                     f"dw_router[{e}] against the oracle's dz")
+    assert_close_rel(np.array([float(b.dbias[e])]), np.array([col.sum()]), TOL, f"dbias[{e}] against the oracle's dz")
     say("m1-width training pass: sampled parity within tolerance")
